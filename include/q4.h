@@ -1,0 +1,153 @@
+/*
+ * q4.h -- C ABI of the GGUF Q4_0 hot-path library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What it computes.  The pages ("Implémentation en Rust du modèle Voxtral
+ * Mini 4B Realtime de Mistral pour l'exécuter dans le navigateur", and its
+ * es/id/hi copies) run the quantised speech model from a GGUF Q4_0 file:
+ * section "Architecture" names the Q4_0 path and the encoder (width 1280) and
+ * decoder (width 3072, GQA 32Q/8KV) whose projections it feeds; section
+ * "Solutions techniques pour l'exécution dans le navigateur", item 3, keeps the
+ * 131072-row token-embedding table as Q4 on the GPU with a row lookup.  Every
+ * projection is y = deq(W) x, the LM head is its argmax, the embedding lookup
+ * is a gather of decoded rows.
+ *
+ * Q4_0 layout (GGUF convention; the pages name the format but do not spell it
+ * out).  A row of K weights (K a multiple of 32) is K/32 blocks of 18 bytes,
+ * rows stored back to back (row stride 18*K/32 bytes).  Block: IEEE binary16
+ * scale d, little-endian, in bytes 0-1; bytes 2..17 hold qs[0..15].  Weight j
+ * of the block (j < 16) is the low nibble of qs[j], weight j+16 the high
+ * nibble; its value is (q - 8) * d.  The byte array is used as stored, never
+ * repacked.
+ *
+ * Conventions for every entry point below.
+ *  - Pointers named w_q4, table_q4, x, y, out, ids, workspace are DEVICE
+ *    pointers; the caller owns every buffer.  The library never allocates,
+ *    frees or synchronises.
+ *  - All device pointers must be 16-byte aligned (Q4_ERR_ALIGN otherwise).
+ *  - Dense matrices are row-major and contiguous: x is [M, K] floats, y is
+ *    [M, N] floats.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *    call only enqueues work on it and returns.
+ *  - Arguments are validated before any HIP call; on a validation error
+ *    nothing is enqueued.  A failed launch returns Q4_ERR_HIP and
+ *    q4_last_hip_error() gives the hipError_t.  Values outside the documented
+ *    ranges that live in device memory (token ids) cannot be checked on the
+ *    host and are handled on the device as stated per call.
+ *  - Calls are thread-safe; the only global state is a per-device cache of
+ *    device properties.
+ */
+#ifndef Q4MI_Q4_H
+#define Q4MI_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int q4_status;
+
+enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    Q4_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 32 != 0            */
+    Q4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned           */
+    Q4_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+    Q4_ERR_HIP = 5        /* a HIP call failed; see q4_last_hip_error()        */
+};
+
+/* Version of this ABI (bumped on any incompatible change). */
+int q4_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* q4_status_string(q4_status status);
+
+/* hipError_t of the most recent Q4_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int q4_last_hip_error(void);
+
+/* Bytes of one Q4_0 row of K weights: 18*K/32.  Returns 0 if K is not a
+ * positive multiple of 32. */
+size_t q4_row_bytes(int64_t K);
+
+/*
+ * q4_matvec -- decode-step projection (the per-token decoder projections of
+ * section "Architecture"): y[m, n] = sum_k deq(W)[n, k] * x[m, k].
+ *   w_q4 : N rows of Q4_0, N*18*K/32 bytes.
+ *   x    : [M, K] float32.    y : [M, N] float32 (written, not accumulated).
+ *   1 <= M <= 8, N >= 1, K a positive multiple of 32, N*K < 2^40.
+ * Float32 products of the exactly decoded weights with x, float32
+ * accumulation.  Tuned for M = 1; rows of x beyond the first re-stream W.
+ * Results are deterministic (fixed reduction order).
+ */
+q4_status q4_matvec(const void* w_q4, const float* x, float* y,
+                    int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_matmul -- prefill / encoder projection (section "Architecture": encoder
+ * width 1280, the 4x-downsample adapter, the decoder's 38/76-token prefix of
+ * section "Correction du padding Q4"): Y = X * deq(W)^T.
+ *   w_q4 : N rows of Q4_0.  x : [M, K] float32.  y : [M, N] float32.
+ *   1 <= M <= 65535*128, 1 <= N < 2^31, K a positive multiple of 32.
+ * Weights and activations are rounded to binary16 (round to nearest even) and
+ * multiplied on the matrix cores with float32 accumulation, so |x| must stay
+ * below 65504.  Deterministic.
+ */
+q4_status q4_matmul(const void* w_q4, const float* x, float* y,
+                    int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_embed_rows -- token-embedding lookup (section "Solutions techniques pour
+ * l'exécution dans le navigateur", item 3): out[i, :] = deq(T[ids[i], :]).
+ *   table_q4 : N rows of Q4_0 (N = vocabulary size, K = model width).
+ *   ids      : M int32 token ids (device memory).
+ *   out      : [M, K] float32; the decoded values are exact.
+ *   M >= 1, N >= 1, K a positive multiple of 32.
+ * An id outside [0, N) yields a row of zeros; the table is never read out of
+ * bounds.
+ */
+q4_status q4_embed_rows(const void* table_q4, const int32_t* ids, float* out,
+                        int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_lmhead_argmax -- greedy next-token choice over the LM head (the same
+ * 131072-row table read as a matrix): out_idx[m] = the lowest n attaining
+ * max_n sum_k deq(T)[n, k] * x[m, k], out_val[m] that maximum (float32, same
+ * arithmetic as q4_matvec).
+ *   w_q4    : N rows of Q4_0.   x : [M, K] float32.
+ *   out_idx : M int32 (device).  out_val : M float32 (device) or NULL.
+ *   workspace, ws_bytes : device scratch of at least
+ *             q4_lmhead_argmax_workspace_bytes(M, N, K) bytes.  It must be
+ *             zero before the first call; every call leaves it zero again, so
+ *             one zero-fill at allocation suffices.  Calls that share a
+ *             workspace must be ordered (same stream or synchronised).
+ *   1 <= M <= 64, 1 <= N < 2^31, K a positive multiple of 32.
+ * Logits that are NaN are never selected.
+ */
+size_t q4_lmhead_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
+q4_status q4_lmhead_argmax(const void* w_q4, const float* x,
+                           int32_t* out_idx, float* out_val,
+                           int64_t M, int64_t N, int64_t K,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * q4_quantize -- device-side GGUF Q4_0 encoder, used to prepare weights:
+ * per block of 32 values, m = the first element of largest magnitude,
+ * d = m / -8 in float32 stored as binary16 (round to nearest even), codes
+ * q = clamp(floor(x / d + 1/2) + 8, 0, 15) decided in float64 against the
+ * stored scale (q = 8 everywhere when it is zero).
+ *   w     : [N, K] float32.   w_q4 : N*18*K/32 bytes (written).
+ *   flag  : device int32 or NULL; set to 1 (never cleared) if any input is
+ *           not finite or a scale overflows binary16 -- the bytes of such a
+ *           block are then unspecified.
+ */
+q4_status q4_quantize(const float* w, void* w_q4, int64_t N, int64_t K,
+                      int32_t* flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MI_Q4_H */

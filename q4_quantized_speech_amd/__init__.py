@@ -1,0 +1,222 @@
+"""q4_quantized_speech_amd -- GGUF Q4_0 hot path for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libq4mi.so`` (declared in
+``include/q4.h``).  PyTorch supplies device memory and the current HIP stream;
+every computation runs in the library's HIP kernels.  There is no CPU
+fallback: if the library is not built, every entry point raises.
+
+Entry points (same names as the C ABI, minus the ``q4_`` prefix):
+    matvec(w_q4, x, out=None)                    y = deq(W) x          (M <= 8)
+    matmul(w_q4, x, out=None)                    Y = X deq(W)^T        (matrix cores)
+    embed_rows(table_q4, ids, out=None)          rows of deq(T)
+    lmhead_argmax(w_q4, x, workspace=None, ...)  argmax_n (deq(T) x)_n
+    quantize(w, out=None, check=True)            float32 -> Q4_0 bytes
+
+Q4_0 tensors are ``torch.uint8`` of shape [N, 18*K/32] (rows of 32-weight
+blocks: binary16 scale + 16 bytes of nibbles, as stored in GGUF).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4mi.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "q4.h")
+
+QK = 32
+BLOCK_BYTES = 18
+
+Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_HIP = range(6)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = f"{where}: {status_string(status)} (status {status}"
+        if status == Q4_ERR_HIP:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg + ")")
+        self.status = status
+        self.hip_error = hip_error
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "q4_abi_version": ([], ctypes.c_int),
+    "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "q4_last_hip_error": ([], ctypes.c_int),
+    "q4_row_bytes": ([_I64], _SZ),
+    "q4_matvec": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "q4_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "q4_embed_rows": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
+    "q4_quantize": ([_P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq4mi.so (built in-tree by q4_quantized_speech_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m q4_quantized_speech_amd.build` "
+                "(there is no CPU fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().q4_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != Q4_OK:
+        raise Q4Error(status, where, lib().q4_last_hip_error() if status == Q4_ERR_HIP else 0)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def q4_shape(w_q4: torch.Tensor):
+    """(N, K) of a Q4_0 tensor of shape [N, 18*K/32]."""
+    if w_q4.dtype != torch.uint8 or w_q4.dim() != 2 or not w_q4.is_contiguous():
+        raise ValueError("Q4_0 weights must be a contiguous uint8 tensor [N, 18*K/32]")
+    n, rb = w_q4.shape
+    if rb % BLOCK_BYTES:
+        raise ValueError(f"row length {rb} is not a multiple of {BLOCK_BYTES}")
+    return n, rb // BLOCK_BYTES * QK
+
+
+def row_bytes(k: int) -> int:
+    return int(lib().q4_row_bytes(k))
+
+
+def _as_2d_f32(x: torch.Tensor, k: int) -> torch.Tensor:
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("activations must be contiguous float32")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"activations must be [M, {k}]")
+    return x
+
+
+def matvec(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """y[m, n] = sum_k deq(W)[n, k] x[m, k] (float32 FMA path); x is [K] or [M, K]."""
+    n, k = q4_shape(w_q4)
+    squeeze = x.dim() == 1
+    x2 = _as_2d_f32(x, k)
+    m = x2.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need_cuda(w_q4, x2, out)
+    _check(lib().q4_matvec(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _stream(stream)), "q4_matvec")
+    return out.view(n) if squeeze else out
+
+
+def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Y = X deq(W)^T on the matrix cores (binary16 operands, float32 accumulation)."""
+    n, k = q4_shape(w_q4)
+    x2 = _as_2d_f32(x, k)
+    m = x2.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need_cuda(w_q4, x2, out)
+    _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _stream(stream)), "q4_matmul")
+    return out
+
+
+def embed_rows(table_q4: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None,
+               stream=None):
+    """out[i, :] = deq(T)[ids[i], :]; ids outside [0, N) give zero rows."""
+    n, k = q4_shape(table_q4)
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 vector")
+    m = ids.shape[0]
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.float32, device=ids.device)
+    _need_cuda(table_q4, ids, out)
+    _check(lib().q4_embed_rows(_ptr(table_q4), _ptr(ids), _ptr(out), m, n, k, _stream(stream)),
+           "q4_embed_rows")
+    return out
+
+
+def lmhead_workspace(m: int, device) -> torch.Tensor:
+    """A zero-filled workspace for lmhead_argmax (reusable across calls)."""
+    nbytes = int(lib().q4_lmhead_argmax_workspace_bytes(m, 0, 0))
+    if nbytes == 0:
+        raise ValueError("M out of range for lmhead_argmax")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def lmhead_argmax(w_q4: torch.Tensor, x: torch.Tensor, workspace: torch.Tensor | None = None,
+                  out_idx: torch.Tensor | None = None, out_val: torch.Tensor | None = None,
+                  stream=None):
+    """(idx, val): per row of x, the lowest n maximising (deq(T) x)_n and that maximum."""
+    n, k = q4_shape(w_q4)
+    x2 = _as_2d_f32(x, k)
+    m = x2.shape[0]
+    if workspace is None:
+        workspace = lmhead_workspace(m, x.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    if out_val is None:
+        out_val = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need_cuda(w_q4, x2, workspace, out_idx, out_val)
+    _check(lib().q4_lmhead_argmax(_ptr(w_q4), _ptr(x2), _ptr(out_idx), _ptr(out_val), m, n, k,
+                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+           "q4_lmhead_argmax")
+    return out_idx, out_val
+
+
+def quantize(w: torch.Tensor, out: torch.Tensor | None = None, check: bool = True, stream=None):
+    """GGUF Q4_0 encoding of a float32 [N, K] tensor on the GPU."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 [N, K] tensor")
+    n, k = w.shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    if out is None:
+        out = torch.empty((n, k // QK * BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    flag = torch.zeros(4, dtype=torch.int32, device=w.device) if check else None
+    _need_cuda(w, out, flag)
+    _check(lib().q4_quantize(_ptr(w), _ptr(out), n, k, _ptr(flag), _stream(stream)), "q4_quantize")
+    if check and int(flag[0].item()) != 0:
+        raise ValueError("q4_quantize: non-finite input or a scale overflowing binary16")
+    return out
+
+
+def declared_symbols(header: str = HEADER):
+    """Function names declared in include/q4.h."""
+    import re
+    with open(header) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))

@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/q4.h declares, and rejects bad arguments before making
+any HIP call (validation returns before the first HIP call by contract)."""
+
+import ctypes
+import os
+
+import pytest
+
+import q4_quantized_speech_amd as q4
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4mi.so not built")
+
+A = 0x10000  # fake, 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_exports_every_declared_symbol():
+    names = q4.declared_symbols()
+    assert "q4_matvec" in names and "q4_lmhead_argmax" in names
+    handle = ctypes.CDLL(q4.LIB_PATH)
+    missing = [n for n in names if not hasattr(handle, n)]
+    assert not missing, missing
+    assert set(names) == set(q4._SIGS), "binding signatures out of sync with the header"
+
+
+def test_basic_queries():
+    lib = q4.lib()
+    assert lib.q4_abi_version() == 1
+    assert lib.q4_row_bytes(3072) == 1728
+    assert lib.q4_row_bytes(32) == 18
+    assert lib.q4_row_bytes(48) == 0
+    assert lib.q4_row_bytes(0) == 0
+    for s in range(6):
+        assert q4.status_string(s)
+    assert lib.q4_lmhead_argmax_workspace_bytes(1, 131072, 3072) > 0
+    assert lib.q4_lmhead_argmax_workspace_bytes(0, 131072, 3072) == 0
+    assert lib.q4_lmhead_argmax_workspace_bytes(65, 131072, 3072) == 0
+
+
+@pytest.mark.parametrize("fn", ["q4_matvec", "q4_matmul", "q4_embed_rows"])
+def test_null_shape_align(fn):
+    f = getattr(q4.lib(), fn)
+    assert f(None, A, A, 1, 16, 64, None) == q4.Q4_ERR_NULL
+    assert f(A, None, A, 1, 16, 64, None) == q4.Q4_ERR_NULL
+    assert f(A, A, None, 1, 16, 64, None) == q4.Q4_ERR_NULL
+    assert f(A, A, A, 1, 16, 48, None) == q4.Q4_ERR_SHAPE     # K % 32
+    assert f(A, A, A, 1, 16, 0, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, A, 0, 16, 64, None) == q4.Q4_ERR_SHAPE     # M = 0
+    assert f(A, A, A, 1, 0, 64, None) == q4.Q4_ERR_SHAPE      # N = 0
+    assert f(A, A, A, -1, 16, 64, None) == q4.Q4_ERR_SHAPE
+    assert f(A + 4, A, A, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
+    assert f(A, A + 8, A, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
+    assert f(A, A, A + 2, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
+
+
+def test_matvec_m_range():
+    f = q4.lib().q4_matvec
+    assert f(A, A, A, 9, 16, 64, None) == q4.Q4_ERR_SHAPE
+
+
+def test_lmhead_argmax_validation():
+    f = q4.lib().q4_lmhead_argmax
+    ws = q4.lib().q4_lmhead_argmax_workspace_bytes(1, 64, 64)
+    assert f(None, A, A, None, 1, 64, 64, A, ws, None) == q4.Q4_ERR_NULL
+    assert f(A, A, None, None, 1, 64, 64, A, ws, None) == q4.Q4_ERR_NULL
+    assert f(A, A, A, None, 0, 64, 64, A, ws, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, A, None, 65, 64, 64, A, ws, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, A, None, 1, 64, 40, A, ws, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, A, None, 1, 64, 64, None, ws, None) == q4.Q4_ERR_WORKSPACE
+    assert f(A, A, A, None, 1, 64, 64, A, ws - 1, None) == q4.Q4_ERR_WORKSPACE
+    assert f(A, A, A, A + 4, 1, 64, 64, A, ws, None) == q4.Q4_ERR_ALIGN
+    assert f(A, A, A, None, 1, 64, 64, A + 8, ws, None) == q4.Q4_ERR_ALIGN
+
+
+def test_quantize_validation():
+    f = q4.lib().q4_quantize
+    assert f(None, A, 4, 64, None, None) == q4.Q4_ERR_NULL
+    assert f(A, None, 4, 64, None, None) == q4.Q4_ERR_NULL
+    assert f(A, A, 0, 64, None, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, 4, 33, None, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A + 1, 4, 64, None, None) == q4.Q4_ERR_ALIGN
+    assert f(A, A, 4, 64, A + 2, None) == q4.Q4_ERR_ALIGN
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        q4.q4_shape(torch.zeros((4, 17), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        q4.q4_shape(torch.zeros((4, 18), dtype=torch.int8))
+    with pytest.raises(ValueError):
+        q4.matvec(torch.zeros((4, 18), dtype=torch.uint8), torch.zeros(32))  # CPU tensors

@@ -1,0 +1,332 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: decoded values bit-exact; q4_matvec within 1e-4*B + 1e-6 per element and
+q4_matmul within 2e-3*B + 1e-5, with B = sum_k |w_k x_k| over the exact
+weights; argmax indices equal wherever the oracle's top-2 margin exceeds the
+two leaders' tolerances (otherwise any row within tolerance of the maximum);
+the encoder byte-for-byte.  Shapes follow the decoder (3072), encoder (1280),
+adapter (5120 -> 3072) and 131072-row vocabulary of the model the pages run.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_checks as oc
+import q4_quantized_speech_amd as q4
+from gpu_util import (announce, assert_within, dev, host, lm_table, needs_gpu, quantize_panels,
+                      weights_q4)
+from oracle import q4_oracle as O
+from q4_quantized_speech_amd import synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+MV = (O.MATVEC_REL, O.MATVEC_ABS)
+MF = (O.MFMA_REL, O.MFMA_ABS)
+
+
+def _rand_w(n, k, seed, scale=0.02):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (g.standard_normal((n, k)) * scale).astype(np.float32)
+
+
+def _rand_x(m, k, seed):
+    return synth.activations(m, k, seed)
+
+
+# --------------------------------------------------------------------------
+# Encoder (device-side quantizer): byte-for-byte
+# --------------------------------------------------------------------------
+
+def test_quantize_bit_exact_random():
+    g = np.random.Generator(np.random.PCG64(101))
+    parts = [
+        _rand_w(257, 3072, 1),
+        (g.standard_normal((64, 256)) * np.exp2(g.integers(-30, 12, (64, 1)))).astype(np.float32),
+        (g.integers(-16, 17, (64, 256)) * 0.25).astype(np.float32),   # exact ties
+        np.zeros((2, 256), np.float32),
+    ]
+    for i, w in enumerate(parts):
+        announce(f"quantize part {i} shape {w.shape}")
+        got = host(q4.quantize(dev(w)))
+        want = O.quantize_q4_0(w)
+        assert np.array_equal(got, want), f"part {i}: {int((got != want).sum())} bytes differ"
+
+
+def test_quantize_golden_blocks():
+    for gb in oc.load_golden():
+        announce(f"quantize golden {gb['name']}")
+        got = host(q4.quantize(dev(gb["x"][None, :]))).tobytes()
+        assert got == gb["bytes"], gb["name"]
+
+
+def test_quantize_flags_nonfinite():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 40] = np.inf
+    announce("quantize inf flag")
+    with pytest.raises(ValueError):
+        q4.quantize(dev(w))
+    w = np.zeros((1, 32), np.float32)
+    w[0, 3] = 6.0e5                                   # scale overflows binary16
+    with pytest.raises(ValueError):
+        q4.quantize(dev(w))
+
+
+# --------------------------------------------------------------------------
+# Embedding rows: exact decode
+# --------------------------------------------------------------------------
+
+def test_embed_golden_blocks_bit_exact():
+    gold = oc.load_golden()
+    table = np.frombuffer(b"".join(gb["bytes"] for gb in gold), np.uint8).reshape(len(gold), 18)
+    ids = np.arange(len(gold), dtype=np.int32)
+    announce("embed golden")
+    got = host(q4.embed_rows(dev(table), dev(ids)))
+    for i, gb in enumerate(gold):
+        assert np.array_equal(got[i].view(np.uint32), gb["deq"].view(np.uint32)), gb["name"]
+
+
+@pytest.mark.parametrize("n,k", [(300, 3072), (77, 96), (50, 160), (9, 32)])
+def test_embed_bit_exact(n, k):
+    qb = O.quantize_q4_0(_rand_w(n, k, 7 + k))
+    ids = np.array([0, n - 1, 5 % n, -1, n, 2**31 - 1, 3 % n, 0], np.int32)
+    announce(f"embed n={n} k={k}")
+    got = host(q4.embed_rows(dev(qb), dev(ids)))
+    want = O.embed_rows(qb, ids, n, k)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_embed_full_table_prefix():
+    table = lm_table()
+    ids = synth.token_ids(synth.PREFIX_TOKENS, synth.seed_for(2, 2))
+    announce("embed full table, 38 ids")
+    got = host(q4.embed_rows(dev(table), dev(ids)))
+    want = O.embed_rows(table, ids, synth.VOCAB, synth.DEC_DIM)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# q4_matvec (float32 FMA path)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(64, 3072), (40, 96), (33, 160), (17, 32), (5, 9216)])
+def test_matvec_one_hot_bit_exact(n, k):
+    qb = O.quantize_q4_0(_rand_w(n, k, 3 + n))
+    w = O.dequantize_q4_0(qb, n, k)
+    wq = dev(qb)
+    for col in [0, 1, 15, 16, 31, k // 2 + 3, k - 1]:
+        x = np.zeros(k, np.float32)
+        x[col] = 1.0
+        announce(f"matvec one-hot n={n} k={k} col={col}")
+        y = host(q4.matvec(wq, dev(x)))
+        assert np.array_equal(y, w[:, col]), col
+
+
+def test_matvec_integer_exact():
+    wi, xi = oc.integer_weight_case(31, 96, 3072, 4)
+    qb = O.quantize_q4_0(wi)
+    ref = xi.astype(np.int64) @ wi.astype(np.int64).T
+    announce("matvec integer exact")
+    for m in range(4):
+        y = host(q4.matvec(dev(qb), dev(xi[m])))
+        assert np.array_equal(y.astype(np.float64), ref[m].astype(np.float64))
+
+
+@pytest.mark.parametrize("n,k,m", [
+    (3072, 3072, 1), (1, 64, 1), (17, 64, 1), (100, 96, 1), (129, 160, 2), (257, 320, 1),
+    (1000, 1280, 1), (64, 15360, 1), (16, 16384, 1), (300, 4096, 8), (513, 9216, 3), (31, 32, 5)])
+def test_matvec_parity(n, k, m):
+    qb = O.quantize_q4_0(_rand_w(n, k, n * 7 + k))
+    x = _rand_x(m, k, 5 + m)
+    announce(f"matvec n={n} k={k} m={m}")
+    y = host(q4.matvec(dev(qb), dev(x)))
+    ref, b = O.matmul_f64(qb, x, n, k)
+    assert_within(y, ref, b, *MV, f"matvec {n}x{k} M={m}")
+
+
+@pytest.mark.parametrize("name,n,k", synth.DECODER_LAYER)
+def test_matvec_decoder_layer_full(name, n, k):
+    """One decode step of a decoder layer at its real shapes, all outputs."""
+    t = [p[0] for p in synth.DECODER_LAYER].index(name)
+    qb = weights_q4(n, k, synth.seed_for(1, t))
+    x = synth.activations(1, k, synth.seed_for(1, 10 + t))[0]
+    announce(f"matvec decoder {name} {n}x{k}")
+    y = host(q4.matvec(dev(qb), dev(x)))
+    ref, b = O.matvec_f64(qb, x, n, k)
+    assert_within(y, ref, b, *MV, f"decoder {name}")
+
+
+def test_matvec_single_3072():
+    qb = weights_q4(3072, 3072, synth.seed_for(0, 0))
+    x = synth.activations(1, 3072, synth.seed_for(0, 1))[0]
+    announce("matvec 3072x3072")
+    y = host(q4.matvec(dev(qb), dev(x)))
+    ref, b = O.matvec_f64(qb, x, 3072, 3072)
+    assert_within(y, ref, b, *MV, "matvec 3072")
+
+
+# --------------------------------------------------------------------------
+# q4_matmul (binary16 operands on the matrix cores, float32 accumulation)
+# --------------------------------------------------------------------------
+
+def test_matmul_one_hot_f16():
+    n, k = 150, 256
+    w = _rand_w(n, k, 77)
+    # make one row carry example D's 0.0624847... code so the tie-to-even shows
+    qb = O.quantize_q4_0(w)
+    wd = O.dequantize_q4_0(qb, n, k)
+    x = np.zeros((k, k), np.float32)
+    np.fill_diagonal(x, 1.0)
+    announce("matmul one-hot")
+    y = host(q4.matmul(dev(qb), dev(x)))
+    assert np.array_equal(y, O.round_f16(wd.T))
+
+
+def test_matmul_golden_f16_rounding():
+    gold = {g["name"]: g for g in oc.load_golden()}
+    d = gold["D"]
+    qb = np.frombuffer(d["bytes"], np.uint8).reshape(1, 18)
+    x = np.zeros((32, 32), np.float32)
+    np.fill_diagonal(x, 1.0)
+    announce("matmul golden D")
+    y = host(q4.matmul(dev(qb), dev(x)))[:, 0]
+    for i, v in d["f16"].items():
+        assert y[i] == v, (i, y[i], v)
+
+
+def test_matmul_integer_exact():
+    for (n, k, m) in [(96, 3072, 40), (130, 256, 129), (16, 1280, 16)]:
+        wi, xi = oc.integer_weight_case(41 + m, n, k, m)
+        qb = O.quantize_q4_0(wi)
+        ref = xi.astype(np.int64) @ wi.astype(np.int64).T
+        announce(f"matmul integer exact {m}x{n}x{k}")
+        y = host(q4.matmul(dev(qb), dev(xi)))
+        assert np.array_equal(y.astype(np.float64), ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 64, 64), (2, 17, 96), (15, 129, 160), (16, 128, 256), (17, 130, 32), (130, 255, 1280),
+    (300, 64, 3072), (3, 3000, 128), (257, 257, 288)])
+def test_matmul_parity_small(m, n, k):
+    qb = O.quantize_q4_0(_rand_w(n, k, m + n + k))
+    x = _rand_x(m, k, 9 + m)
+    announce(f"matmul m={m} n={n} k={k}")
+    y = host(q4.matmul(dev(qb), dev(x)))
+    ref, b = O.matmul_f64(qb, x, n, k)
+    assert_within(y, ref, b, *MF, f"matmul {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [16, 38, 76])
+def test_matmul_decoder_prefix_full(m):
+    """The decoder projection set at the prefix lengths 16 / 38 / 76."""
+    x_all = synth.activations(m, 9216, synth.seed_for(3, 20 + m))
+    for t, (name, n, k) in enumerate(synth.DECODER_LAYER):
+        qb = weights_q4(n, k, synth.seed_for(1, t))
+        x = np.ascontiguousarray(x_all[:, :k])
+        announce(f"matmul prefix M={m} {name} {n}x{k}")
+        y = host(q4.matmul(dev(qb), dev(x)))
+        ref, b = O.matmul_f64(qb, x, n, k)
+        assert_within(y, ref, b, *MF, f"prefix M={m} {name}")
+
+
+@pytest.mark.parametrize("m", [375, 1500, 3000])
+def test_matmul_encoder_full(m):
+    """Encoder projections (width 1280) and the adapter at floor(M/4) frames."""
+    shapes = [(name, n, k, m) for (name, n, k) in synth.ENCODER_LAYER]
+    shapes.append((synth.ADAPTER[0], synth.ADAPTER[1], synth.ADAPTER[2], m // 4))
+    for t, (name, n, k, mm) in enumerate(shapes):
+        qb = weights_q4(n, k, synth.seed_for(4, t))
+        x = synth.activations(mm, k, synth.seed_for(4, 10 + t))
+        announce(f"matmul encoder M={mm} {name} {n}x{k}")
+        y = host(q4.matmul(dev(qb), dev(x)))
+        ref, b = O.matmul_f64(qb, x, n, k)
+        assert_within(y, ref, b, *MF, f"encoder M={mm} {name}")
+
+
+# --------------------------------------------------------------------------
+# q4_lmhead_argmax
+# --------------------------------------------------------------------------
+
+def test_lmhead_ties_and_planted():
+    n, k = 5000, 256
+    w = _rand_w(n, k, 123)
+    x = _rand_x(3, k, 124)
+    # row 4321 is a clear winner for x[0]; rows 17 and 900 tie for x[1]
+    w[4321] = np.float32(0.02) * np.sign(x[0])
+    w[17] = w[900] = np.float32(0.03) * np.sign(x[1])
+    qb = O.quantize_q4_0(w)
+    announce("lmhead ties/planted M=3")
+    idx, val = q4.lmhead_argmax(dev(qb), dev(x))
+    idx, val = host(idx), host(val)
+    assert idx[0] == 4321
+    assert idx[1] == 17                        # lowest of two bit-identical rows
+    for i in range(3):
+        y, b = O.lmhead_logits(qb, x[i], n, k)
+        assert O.argmax_accepts(y, b, int(idx[i])), i
+        assert abs(val[i] - y[idx[i]]) <= O.MATVEC_REL * b[idx[i]] + O.MATVEC_ABS
+
+
+def test_lmhead_workspace_reuse_and_odd_k():
+    n, k = 700, 96
+    qb = O.quantize_q4_0(_rand_w(n, k, 5))
+    ws = q4.lmhead_workspace(1, "cuda")
+    wq = dev(qb)
+    for s in range(4):
+        x = _rand_x(1, k, 300 + s)
+        announce(f"lmhead reuse {s}")
+        idx, _ = q4.lmhead_argmax(wq, dev(x), workspace=ws)
+        y, b = O.lmhead_logits(qb, x[0], n, k)
+        assert O.argmax_accepts(y, b, int(host(idx)[0]))
+    assert int(host(ws).astype(np.int64).sum()) >= 0
+    assert np.all(host(ws)[:256] == 0)            # counters back to zero
+
+
+def test_lmhead_full_table():
+    table = lm_table()
+    x = synth.activations(1, synth.DEC_DIM, synth.seed_for(2, 1))
+    announce("lmhead full table")
+    idx, val = q4.lmhead_argmax(dev(table), dev(x))
+    i = int(host(idx)[0])
+    y, b = O.lmhead_logits(table, x[0], synth.VOCAB, synth.DEC_DIM)
+    assert O.argmax_accepts(y, b, i), (i, O.argmax_lowest(y), O.top2_margin(y))
+    assert abs(float(host(val)[0]) - y[i]) <= O.MATVEC_REL * b[i] + O.MATVEC_ABS
+    # the full logit vector of the same kernel family agrees everywhere
+    yy = host(q4.matvec(dev(table), dev(x[0])))
+    assert_within(yy, y, b, *MV, "lmhead logits")
+
+
+# --------------------------------------------------------------------------
+# Determinism and out-of-bounds writes
+# --------------------------------------------------------------------------
+
+def test_determinism():
+    qb = dev(weights_q4(3072, 3072, synth.seed_for(0, 0)))
+    x = dev(synth.activations(76, 3072, 55))
+    announce("determinism")
+    a = host(q4.matvec(qb, x[0]))
+    b = host(q4.matvec(qb, x[0]))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    a = host(q4.matmul(qb, x))
+    b = host(q4.matmul(qb, x))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    i1, v1 = q4.lmhead_argmax(qb, x[:1])
+    i2, v2 = q4.lmhead_argmax(qb, x[:1])
+    assert host(i1)[0] == host(i2)[0] and host(v1)[0] == host(v2)[0]
+
+
+def test_no_write_past_outputs():
+    n, k, m = 130, 96, 3
+    qb = dev(O.quantize_q4_0(_rand_w(n, k, 1)))
+    x = dev(_rand_x(m, k, 2))
+    sentinel = -12345.0
+    announce("canary matvec/matmul/embed")
+    buf = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
+    q4.matvec(qb, x, out=buf[: m * n].view(m, n))
+    assert np.all(host(buf)[m * n:] == sentinel)
+    buf.fill_(sentinel)
+    q4.matmul(qb, x, out=buf[: m * n].view(m, n))
+    assert np.all(host(buf)[m * n:] == sentinel)
+    ids = dev(np.array([1, 2, 129], np.int32))
+    buf = torch.full((3 * k + 64,), sentinel, dtype=torch.float32, device="cuda")
+    q4.embed_rows(qb, ids, out=buf[: 3 * k].view(3, k))
+    assert np.all(host(buf)[3 * k:] == sentinel)

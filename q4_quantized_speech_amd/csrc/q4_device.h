@@ -48,8 +48,8 @@ __device__ __forceinline__ float nib_dot4(uint32_t q, f32x4 xl, f32x4 xh, float 
   uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
   // Keep the masked dwords opaque so each weight costs one v_cvt_f32_ubyteN
   // rather than a bit-field extract plus a convert.
-  asm volatile("" : "+v"(lo));
-  asm volatile("" : "+v"(hi));
+  asm("" : "+v"(lo));
+  asm("" : "+v"(hi));
   acc = __builtin_fmaf(ubyte_f<0>(lo), xl.x, acc);
   acc = __builtin_fmaf(ubyte_f<1>(lo), xl.y, acc);
   acc = __builtin_fmaf(ubyte_f<2>(lo), xl.z, acc);
@@ -72,12 +72,20 @@ __device__ __forceinline__ void load_block_any(const uint8_t* __restrict__ base,
   for (int t = 0; t < 4; ++t) qs[t] = static_cast<uint32_t>(p[1 + 2 * t]) | (static_cast<uint32_t>(p[2 + 2 * t]) << 16);
 }
 
-// Reduction over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
+// row receives the total.  quad_perm swaps lanes within quads, then two row
+// rotations fold the four quad sums.  The add order is the same in every row.
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 8, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 1, 16);
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x128>(v);  // row_ror:8
   return v;
 }
 

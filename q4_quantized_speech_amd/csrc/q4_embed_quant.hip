@@ -72,7 +72,10 @@ __global__ __launch_bounds__(EQ_THREADS) void quantize_kernel(const float* __res
     bad |= !(a <= 3.402823466e38f);  // inf or NaN
     if (a > amax) { amax = a; m = v[i]; }
   }
-  const float d = m / -8.0f;
+  float d = m / -8.0f;
+  // Keep the division and the binary16 conversion separate: fused into one
+  // mixed-precision FMA with a +0 addend, m = +0 would give +0 instead of -0.
+  asm volatile("" : "+v"(d));
   const _Float16 dh = static_cast<_Float16>(d);
   uint16_t dbits;
   __builtin_memcpy(&dbits, &dh, 2);

@@ -1,25 +1,30 @@
-// Q4_0 matrix-vector product (decode step, M = 1) and the LM-head argmax.
+// Q4_0 matrix-vector product (decode step) and the LM-head argmax.
 //
 // Section "Architecture" of "Implémentation en Rust du modèle Voxtral Mini 4B
 // Realtime de Mistral pour l'exécuter dans le navigateur": every decoder
 // projection runs on Q4_0 weights; per generated token each weight byte is read
 // once, so this kernel is an HBM stream.  Design for gfx950:
-//  * the weight matrix is read as 36-byte block pairs (two Q4_0 blocks; a pair
-//    whose first block has an even flat index is dword aligned), 16 lanes per
-//    row, so each 16-lane DPP row reads 576 contiguous bytes per step;
-//  * x is staged once per workgroup in LDS with the per-block sums
-//    S_b = sum of x over block b, padded to 272 bytes per pair so that the 16
-//    lanes of a row read 16 different pairs without bank conflicts;
-//  * codes are turned into floats with v_cvt_f32_ubyte (one op per weight) and
+//  * a row is read as 36-byte block pairs (two Q4_0 blocks; with K % 64 == 0
+//    every pair is dword aligned).  16 lanes cover 16 consecutive pairs of a
+//    row (576 contiguous bytes per DPP row); the K range is split over
+//    KS = ceil(K / 1024) waves of the workgroup, so every lane owns exactly one
+//    pair column for the whole kernel;
+//  * that lane keeps its 64 x values and the two block sums S_b (sum of x over
+//    block b) in registers: x is read from memory once per lane, never from LDS;
+//  * each lane serves R = 2 rows per pass (4 DPP rows per wave -> 8 rows);
+//    passes are double-buffered with two register sets used alternately, so
+//    the in-order vmcnt counter lets the next pass's loads fly while the
+//    current one computes;
+//  * codes become floats with v_cvt_f32_ubyte (one op per weight) and are
 //    accumulated as sum q*x; the -8 offset is applied per block:
 //    y += d * (sum_j q_j x_j - 8 * S_b);
-//  * the 16 partial sums of a row are reduced inside the DPP row;
-//  * workgroups are persistent (a grid-stride loop over row groups) so x is
-//    staged once per workgroup however tall the matrix is.
-// The argmax variant ("LM head" over the same 131072-row table the embedding
-// lookup of section "Solutions techniques", item 3, reads) keeps the best
-// (value, lowest index) per lane, reduces it per workgroup, and the last
-// workgroup to finish reduces the per-workgroup partials in a fixed order.
+//  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
+//    sums are then added in LDS in a fixed order (deterministic results);
+//  * workgroups are persistent (a grid-stride loop over row groups).
+// The argmax variant (the LM head over the 131072-row table that section
+// "Solutions techniques", item 3, keeps in Q4) tracks the best (value, lowest
+// index) per lane, reduces it per workgroup, and the last workgroup to finish
+// folds the per-workgroup partials in a fixed order.
 
 #include "q4_device.h"
 #include "q4_kernels.h"
@@ -27,77 +32,17 @@
 namespace q4 {
 namespace {
 
-constexpr int MV_THREADS = 256;
-constexpr int XP = 68;                 // floats per staged pair: 64 x + S_0, S_1, pad
-constexpr int MAX_LDS_K = 15360;       // K with (K/64)*272 B <= 64 KiB
 constexpr int AM_MAX_PARTIALS = 2048;  // per-row partials of the argmax reduction
+constexpr int MV_R = 2;                // rows per lane per pass
 
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
-// Stage x[0..K) and the block sums into LDS (layout: pair c at xs + 68c).
-__device__ __forceinline__ void stage_x(const float* __restrict__ x, float* xs, int nb) {
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(b) * QK);
-    float* dst = xs + (b >> 1) * XP + (b & 1) * QK;
-    f32x4 v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = src[t];
-    f32x4 s4 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-#pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 4 * t) = v[t];
-    xs[(b >> 1) * XP + 64 + (b & 1)] = (s4.x + s4.y) + (s4.z + s4.w);
-  }
-}
-
-// One block pair of one row against the staged x: returns
-// d0*(sum q x - 8 S0) + d1*(sum q x - 8 S1) for R rows at once.
-template <int R>
-__device__ __forceinline__ void pair_dot(const uint32_t (&w)[R][9], const float* xp, float (&acc)[R]) {
-  float s0[R], s1[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const f32x4 xl = *reinterpret_cast<const f32x4*>(xp + 4 * t);
-    const f32x4 xh = *reinterpret_cast<const f32x4*>(xp + 16 + 4 * t);
-#pragma unroll
-    for (int r = 0; r < R; ++r) s0[r] = nib_dot4(shift16(w[r][t + 1], w[r][t]), xl, xh, s0[r]);
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const f32x4 xl = *reinterpret_cast<const f32x4*>(xp + 32 + 4 * t);
-    const f32x4 xh = *reinterpret_cast<const f32x4*>(xp + 48 + 4 * t);
-#pragma unroll
-    for (int r = 0; r < R; ++r) s1[r] = nib_dot4(w[r][5 + t], xl, xh, s1[r]);
-  }
-  const float S0 = xp[64], S1 = xp[65];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float d0 = half_bits_to_float(w[r][0] & 0xFFFFu);
-    const float d1 = half_bits_to_float(w[r][4] >> 16);
-    acc[r] = __builtin_fmaf(d0, __builtin_fmaf(-8.f, S0, s0[r]), acc[r]);
-    acc[r] = __builtin_fmaf(d1, __builtin_fmaf(-8.f, S1, s1[r]), acc[r]);
-  }
-}
-
-template <int R>
-__device__ __forceinline__ void load_pairs(const uint8_t* __restrict__ W, const int64_t (&row)[R],
-                                           const bool (&ok)[R], int64_t row_bytes, int c,
-                                           uint32_t (&w)[R][9]) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (ok[r]) {
-      const uint8_t* p = W + row[r] * row_bytes + static_cast<int64_t>(c) * PAIR_BYTES;
-      const u32x4a a = *reinterpret_cast<const u32x4a*>(p);
-      const u32x4a b = *reinterpret_cast<const u32x4a*>(p + 16);
-      w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
-      w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
-      w[r][8] = *reinterpret_cast<const uint32_t*>(p + 32);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 9; ++t) w[r][t] = 0u;
-    }
-  }
+__device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t (&w)[9]) {
+  const u32x4a a = *reinterpret_cast<const u32x4a*>(p);
+  const u32x4a b = *reinterpret_cast<const u32x4a*>(p + 16);
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
 }
 
 // Argmax bookkeeping: idx < 0 means "no candidate"; NaN never wins.
@@ -108,9 +53,8 @@ __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
 
 // Fold the candidates of all threads of the workgroup; result valid in thread 0.
 __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
-  __shared__ float sv[MV_THREADS / 16];
-  __shared__ int si[MV_THREADS / 16];
-  // within a 16-lane row
+  __shared__ float sv[64];
+  __shared__ int si[64];
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 16);
@@ -161,58 +105,140 @@ __device__ __forceinline__ void am_finish(float bv, int bi, int m, int32_t* out_
   }
 }
 
-// Pair kernel: K % 64 == 0 and K <= MAX_LDS_K.  Each wave holds 4 groups of
-// 16 lanes; group g handles R rows; a pass of the workgroup covers 16R rows.
-template <int R, bool ARGMAX>
-__global__ __launch_bounds__(MV_THREADS) void matvec_pairs_kernel(
+// Pair kernel: K % 64 == 0, K <= 12288, KS = ceil(K / 1024) waves per workgroup.
+template <int KS, bool ARGMAX>
+__global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
     int K) {
-  extern __shared__ float xs[];
+  constexpr int R = MV_R;
+  constexpr int ROWS = 4 * R;  // rows per pass
+  __shared__ float red[2][KS][ROWS];
   const int m = blockIdx.y;
-  const int nb = K / QK, nbp = nb / 2;
-  const int64_t row_bytes = static_cast<int64_t>(nbp) * PAIR_BYTES;
-  stage_x(X + static_cast<int64_t>(m) * K, xs, nb);
-  __syncthreads();
+  const int nbp = K >> 6;
+  const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
+  const int tid = threadIdx.x;
+  const int ks = tid >> 6, j = tid & 15, grp = (tid >> 4) & 3;
+  const int craw = j + 16 * ks;
+  const bool cvalid = craw < nbp;
+  const int c = cvalid ? craw : nbp - 1;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS;
 
-  const int j = threadIdx.x & 15;
-  const int grp = threadIdx.x >> 4;  // 0..15 over the workgroup
-  const int64_t rows_per_pass = 16 * R;
+  // weights of the first pass, then this lane's x slice (64 floats) and sums
+  int64_t row0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+  uint32_t wa[R][9], wb[R][9];
+  auto load = [&](int64_t r0, uint32_t (&w)[R][9]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t row = r0 + grp * R + r;
+      row = row < N ? row : N - 1;
+      load_pair(W + row * rb + static_cast<int64_t>(c) * PAIR_BYTES, w[r]);
+    }
+  };
+  load(row0, wa);
+  float xv[64];
+  {
+    const f32x4* xg = reinterpret_cast<const f32x4*>(X + static_cast<int64_t>(m) * K + 64 * c);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const f32x4 v = xg[t];
+      xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
+    }
+  }
+  float S0 = 0.f, S1 = 0.f;
+  {
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) { a0 += xv[t]; a1 += xv[16 + t]; b0 += xv[32 + t]; b1 += xv[48 + t]; }
+    S0 = a0 + a1;
+    S1 = b0 + b1;
+  }
+  if (!cvalid) S0 = S1 = 0.f;
+
+  // sum over this lane's pair for R rows: d0*(sum q x - 8 S0) + d1*(...)
+  auto compute = [&](uint32_t (&w)[R][9], float (&acc)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 xl = {xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
+        const f32x4 xh = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
+        s0 = nib_dot4(shift16(w[r][t + 1], w[r][t]), xl, xh, s0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 xl = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
+        const f32x4 xh = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
+        s1 = nib_dot4(w[r][5 + t], xl, xh, s1);
+      }
+      const float d0 = cvalid ? half_bits_to_float(w[r][0] & 0xFFFFu) : 0.f;
+      const float d1 = cvalid ? half_bits_to_float(w[r][4] >> 16) : 0.f;
+      acc[r] = __builtin_fmaf(d0, __builtin_fmaf(-8.f, S0, s0), 0.f);
+      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(-8.f, S1, s1), acc[r]);
+    }
+  };
+
   float bv = 0.f;
   int bi = -1;
-  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_pass; row0 < N;
-       row0 += static_cast<int64_t>(gridDim.x) * rows_per_pass) {
-    int64_t row[R];
-    bool ok[R];
+  // reduce the pass at r0: DPP row sums, then the KS waves in LDS (buffer q)
+  auto finish = [&](int64_t r0, float (&acc)[R], int q) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = row16_sum(acc[r]);
+    if constexpr (KS > 1) {
+      if (j == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[q][ks][grp * R + r] = acc[r];
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float sum = red[q][0][grp * R + r];
+          for (int u = 1; u < KS; ++u) sum += red[q][u][grp * R + r];
+          acc[r] = sum;
+        }
+      }
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = r0 + grp * R + r;
+        if constexpr (ARGMAX) {
+          if (row < N && am_better(acc[r], static_cast<int>(row), bv, bi)) {
+            bv = acc[r];
+            bi = static_cast<int>(row);
+          }
+        } else {
+          if (row < N && j == 0) Y[static_cast<int64_t>(m) * N + row] = acc[r];
+        }
+      }
+    }
+  };
+
+  if (row0 + stride >= N) {
+    // one pass per workgroup
     float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      row[r] = row0 + grp * R + r;
-      ok[r] = row[r] < N;
-      acc[r] = 0.f;
-    }
-    uint32_t w[R][9];
-    if (j < nbp) load_pairs<R>(W, row, ok, row_bytes, j, w);
-    for (int c = j; c < nbp; c += 16) {
-      uint32_t wn[R][9];
-      const bool more = c + 16 < nbp;
-      if (more) load_pairs<R>(W, row, ok, row_bytes, c + 16, wn);
-      pair_dot<R>(w, xs + c * XP, acc);
-      if (more) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int t = 0; t < 9; ++t) w[r][t] = wn[r][t];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = row16_sum(acc[r]);
-      if constexpr (ARGMAX) {
-        if (ok[r] && am_better(v, static_cast<int>(row[r]), bv, bi)) { bv = v; bi = static_cast<int>(row[r]); }
-      } else {
-        if (ok[r] && j == 0) Y[static_cast<int64_t>(m) * N + row[r]] = v;
-      }
+    compute(wa, acc);
+    finish(row0, acc, 0);
+  } else {
+    // ping-pong over passes; loads past the end are clamped to the last row
+    for (;;) {
+      const int64_t r1 = row0 + stride;
+      load(r1, wb);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      float acc[R];
+      compute(wa, acc);
+      finish(row0, acc, 0);
+      if (r1 >= N) break;
+      const int64_t r2 = r1 + stride;
+      load(r2, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      float acc2[R];
+      compute(wb, acc2);
+      finish(r1, acc2, 1);
+      if (r2 >= N) break;
+      row0 = r2;
     }
   }
   if constexpr (ARGMAX) am_finish(bv, bi, m, out_idx, out_val, workspace);
@@ -221,7 +247,7 @@ __global__ __launch_bounds__(MV_THREADS) void matvec_pairs_kernel(
 // Generic kernel: any K % 32 == 0 (odd block counts, very long rows).  16
 // lanes per row, one block per lane per step, x read from global memory.
 template <bool ARGMAX>
-__global__ __launch_bounds__(MV_THREADS) void matvec_any_kernel(
+__global__ __launch_bounds__(256) void matvec_any_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
     int K) {
@@ -262,35 +288,48 @@ __global__ __launch_bounds__(MV_THREADS) void matvec_any_kernel(
   if constexpr (ARGMAX) am_finish(bv, bi, m, out_idx, out_val, workspace);
 }
 
-int persistent_blocks(int64_t passes, int per_cu) {
+template <int KS, bool ARGMAX>
+void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
+                  int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t rows = 4 * MV_R;
+  const int64_t passes = (N + rows - 1) / rows;
+  // A persistent grid must not exceed what is resident at once: a second,
+  // partial round of workgroups costs far more than it adds.
+  static int per_cu = 0;  // per process; the kernel's resource use is fixed
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX>, 64 * KS,
+                                                      0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
   const int64_t cap = static_cast<int64_t>(device_info().cu_count) * per_cu;
-  return static_cast<int>(passes < cap ? passes : cap);
+  int64_t g = passes < cap ? passes : cap;
+  if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
+  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX>), dim3(static_cast<unsigned>(g), M),
+                     dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
 }
 
 template <bool ARGMAX>
 hipError_t launch_mv(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val,
                      void* ws, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const bool pairs = (K % 64 == 0) && K <= MAX_LDS_K;
-  if (pairs) {
-    const size_t lds = static_cast<size_t>(K / 64) * XP * sizeof(float);
-    // two rows per lane once the matrix is tall enough to keep every CU busy
-    const bool tall = N >= static_cast<int64_t>(device_info().cu_count) * 64;
-    if (tall) {
-      int g = persistent_blocks((N + 31) / 32, 4);
+  // more than 12 waves per workgroup would cap registers below the lane's x slice
+  const int64_t ks = (K % 64 == 0 && K <= 12288) ? (K / 64 + 15) / 16 : 0;
+  switch (ks) {
+#define Q4_MV_CASE(n) \
+  case n: launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
+    Q4_MV_CASE(1) Q4_MV_CASE(2) Q4_MV_CASE(3) Q4_MV_CASE(4) Q4_MV_CASE(5) Q4_MV_CASE(6)
+    Q4_MV_CASE(7) Q4_MV_CASE(8) Q4_MV_CASE(9) Q4_MV_CASE(10) Q4_MV_CASE(11) Q4_MV_CASE(12)
+#undef Q4_MV_CASE
+    default: {
+      const int cu = device_info().cu_count;
+      int64_t g = (N + 15) / 16;
+      const int64_t cap = static_cast<int64_t>(cu) * 8;
+      if (g > cap) g = cap;
       if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
-      hipLaunchKernelGGL((matvec_pairs_kernel<2, ARGMAX>), dim3(g, M), dim3(MV_THREADS), lds, s,
-                         w, x, y, idx, val, ws, N, static_cast<int>(K));
-    } else {
-      int g = persistent_blocks((N + 15) / 16, 4);
-      if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
-      hipLaunchKernelGGL((matvec_pairs_kernel<1, ARGMAX>), dim3(g, M), dim3(MV_THREADS), lds, s,
-                         w, x, y, idx, val, ws, N, static_cast<int>(K));
+      hipLaunchKernelGGL((matvec_any_kernel<ARGMAX>), dim3(static_cast<unsigned>(g), M), dim3(256),
+                         0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
     }
-  } else {
-    int g = persistent_blocks((N + 15) / 16, 8);
-    if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
-    hipLaunchKernelGGL((matvec_any_kernel<ARGMAX>), dim3(g, M), dim3(MV_THREADS), 0, s, w, x, y,
-                       idx, val, ws, N, static_cast<int>(K));
   }
   return hipGetLastError();
 }

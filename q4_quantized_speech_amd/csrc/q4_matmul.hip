@@ -15,18 +15,19 @@
 // (q - 8) * d in binary16 (exact q - 8, one rounding of the product); X is
 // rounded to binary16 (nearest even); accumulation is float32.
 //
-// Main kernel (K % 64 == 0): a 256-thread workgroup owns a 128 (M) x 256 (N)
-// tile of Y; each of its four waves a 64 x 128 sub-tile (4 x 8 MFMA tiles).
-// K advances in stages of 64 (one 36-byte block pair per weight row).  Per
+// Main kernel (K % 64 == 0): a 256-thread workgroup owns a 128 x 128 tile of
+// Y; each of its four waves a 64 x 64 sub-tile (4 x 4 MFMA tiles).  K
+// advances in stages of 64 (one 36-byte block pair per weight row).  Per
 // stage the workgroup converts X and decodes W once into LDS (double
 // buffered, in operand order, so fragments are contiguous 1 KiB LDS rows),
-// while the global loads of the stage after next are already in flight in a
-// second register set (two sets used alternately: no register copies, so the
-// in-order vmcnt counter stays exact).  Tiles are renumbered so each XCD
+// while the global loads of the next three stages are in flight in a ring of
+// three register sets (fixed roles in an unrolled loop: no register copies,
+// so the in-order vmcnt counter stays exact).  64 KiB of LDS per workgroup
+// lets two workgroups share a CU.  Tiles are renumbered so each XCD
 // (8 per chip, each with its own L2) works on a contiguous range of tiles that
 // share rows of X.
 //
-// A simple kernel (128 x 128 tiles, one block per stage) covers any K % 32.
+// A simple kernel (128 x 128 tiles, one block per stage) covers K % 64 == 32.
 
 #include "q4_device.h"
 #include "q4_kernels.h"
@@ -85,19 +86,24 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: 128 x 256 tiles, K % 64 == 0.
+// Main kernel: 128 x 128 tiles, K % 64 == 0.
 // ---------------------------------------------------------------------------
-constexpr int T_BM = 128, T_BN = 256, T_THREADS = 256;
+constexpr int T_BM = 128, T_BN = 128, T_THREADS = 256;
 
+// Stage registers of one thread.  Roles are wave-uniform: waves 0-1 stage
+// block 0 of the pair, waves 2-3 block 1; thread t stages row t % 128 of X
+// and of W for that block.
 struct StageRegs {
-  f32x4 a[8];     // X: row tid/2, 32 floats of block (tid & 1)
-  uint32_t b[9];  // W: row tid, one 36-byte block pair
+  f32x4 a[8];     // X: the 32 floats of the block
+  uint32_t b[5];  // W: the 20 bytes starting at 16 * block within the pair
 };
 
-__global__ __launch_bounds__(T_THREADS) void matmul_tile_kernel(
-    const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y, int M, int N,
-    int K, int tiles_n, int ntiles) {
-  // [buf][block of the pair][16-row tile][lane]
+// Two waves per SIMD is the occupancy target (two workgroups per CU, 64 KiB
+// of LDS each); saying so keeps all accumulators in VGPRs.
+__global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
+                        float* __restrict__ Y, int M, int N, int K, int tiles_n, int ntiles) {
+  // [buf][block of the pair][16-row tile][lane]: 2 x 32 KiB
   __shared__ f16x8 As[2][2][T_BM / 16][64];
   __shared__ f16x8 Bs[2][2][T_BN / 16][64];
 
@@ -112,11 +118,11 @@ __global__ __launch_bounds__(T_THREADS) void matmul_tile_kernel(
   // loader roles.  Rows past M and columns past N are clamped to the last
   // valid one: they only feed outputs that are never stored, so no masking
   // (a mask on loaded data would pull a wait for this stage's loads forward).
-  const int ar = tid >> 1, ah = tid & 1;  // X row within the tile, block of the pair
-  const int am = m0 + ar;
-  const float* xrow = X + static_cast<int64_t>(am < M ? am : M - 1) * K + 32 * ah;
-  const int bn = n0 + tid;
-  const uint8_t* wrow = W + static_cast<int64_t>(bn < N ? bn : N - 1) * rb;
+  const int lr = tid & 127, blk = tid >> 7;  // row within the tile, block of the pair
+  const int am = m0 + lr;
+  const float* xrow = X + static_cast<int64_t>(am < M ? am : M - 1) * K + 32 * blk;
+  const int bn = n0 + lr;
+  const uint8_t* wrow = W + static_cast<int64_t>(bn < N ? bn : N - 1) * rb + 16 * blk;
 
   auto load = [&](int s, StageRegs& r) {
     s = s < nbp ? s : nbp - 1;  // past the end: reload the last stage (unused)
@@ -125,95 +131,106 @@ __global__ __launch_bounds__(T_THREADS) void matmul_tile_kernel(
     for (int u = 0; u < 8; ++u) r.a[u] = xp[u];
     const uint8_t* wp = wrow + static_cast<int64_t>(s) * PAIR_BYTES;
     const u32x4a p0 = *reinterpret_cast<const u32x4a*>(wp);
-    const u32x4a p1 = *reinterpret_cast<const u32x4a*>(wp + 16);
     r.b[0] = p0.x; r.b[1] = p0.y; r.b[2] = p0.z; r.b[3] = p0.w;
-    r.b[4] = p1.x; r.b[5] = p1.y; r.b[6] = p1.z; r.b[7] = p1.w;
-    r.b[8] = *reinterpret_cast<const uint32_t*>(wp + 32);
+    r.b[4] = *reinterpret_cast<const uint32_t*>(wp + 16);
   };
-  auto store = [&](const StageRegs& r, int buf, uint32_t z) {
-    auto zf = [z](f32x4 v) {
-      return f32x4{__uint_as_float(__float_as_uint(v.x) | z), __uint_as_float(__float_as_uint(v.y) | z),
-                   __uint_as_float(__float_as_uint(v.z) | z), __uint_as_float(__float_as_uint(v.w) | z)};
-    };
+
+  // Ordering guard.  The conversion of a register set is pure arithmetic, so
+  // the compiler would hoist it above the barrier to right behind that set's
+  // loads, making the wave wait for loads it has just issued.  The first
+  // operation on every loaded register is therefore a volatile asm VALU op
+  // (the binary16 pack for X, a move for W): volatile asm keeps its place
+  // after the barrier, and everything else depends on it.
+  auto pk_f16 = [](float a, float b) -> uint32_t {
+    uint32_t r;
+    asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  };
+  auto pin = [](uint32_t v) -> uint32_t {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+  };
+
+  auto store = [&](const StageRegs& r, int buf) {
     // X: lane slot (row % 16) + 16 g holds k {4g..4g+3, 16+4g..16+4g+3}
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      As[buf][ah][ar >> 4][(ar & 15) + 16 * g] = cvt8_f16(zf(r.a[g]), zf(r.a[4 + g]));
-    // W: block 0 (scale in the low half of dword 0, codes shifted by 2 bytes),
-    //    block 1 (scale in the high half of dword 4, codes in dwords 5..8)
-    uint32_t b[9];
-#pragma unroll
-    for (int t = 0; t < 9; ++t) b[t] = r.b[t] | z;
-    const uint32_t d0 = b[0] & 0xFFFFu;
-    const uint32_t d1 = b[4] >> 16;
-#pragma unroll
     for (int g = 0; g < 4; ++g) {
-      Bs[buf][0][tid >> 4][(tid & 15) + 16 * g] = decode8_f16(shift16(b[g + 1], b[g]), d0);
-      Bs[buf][1][tid >> 4][(tid & 15) + 16 * g] = decode8_f16(b[5 + g], d1);
+      const f32x4 lo = r.a[g], hi = r.a[4 + g];
+      const u32x4a h = {pk_f16(lo.x, lo.y), pk_f16(lo.z, lo.w), pk_f16(hi.x, hi.y), pk_f16(hi.z, hi.w)};
+      *reinterpret_cast<u32x4a*>(&As[buf][blk][lr >> 4][(lr & 15) + 16 * g]) = h;
+    }
+    uint32_t b[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) b[t] = pin(r.b[t]);
+    if (blk == 0) {  // wave-uniform: bytes 0..19 = scale, codes at byte 2
+      const uint32_t d = b[0] & 0xFFFFu;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        Bs[buf][0][lr >> 4][(lr & 15) + 16 * g] = decode8_f16(shift16(b[g + 1], b[g]), d);
+    } else {         // bytes 16..35 = (2 bytes of block 0), scale, codes at byte 4
+      const uint32_t d = b[0] >> 16;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        Bs[buf][1][lr >> 4][(lr & 15) + 16 * g] = decode8_f16(b[g + 1], d);
     }
   };
 
-  f32x4v acc[4][8];
+  f32x4v acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f16x8 a[4], b[8];
+    for (int bk = 0; bk < 2; ++bk) {
+      f16x8 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[buf][blk][wm * 4 + i][lane];
+      for (int i = 0; i < 4; ++i) a[i] = As[buf][bk][wm * 4 + i][lane];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = Bs[buf][blk][wn * 8 + j][lane];
+      for (int j = 0; j < 4; ++j) b[j] = Bs[buf][bk][wn * 4 + j][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  // Ordering guard.  The conversion of a register set is pure arithmetic, so
-  // the compiler may hoist it above the barrier to right behind that set's
-  // loads, making the wave wait for loads it has just issued.  The conversion
-  // ORs its inputs with a zero read from LDS after the barrier, which ties it
-  // below that point without reading the set any earlier.
-  // The word is read inline through the LDS variable, not volatile and not
-  // through a lambda capture: either would make it a flat load, which counts
-  // on vmcnt and would wait for the global loads.  The stored value is a
-  // runtime zero (K > 0) so the compiler cannot fold the reads, and a read
-  // after a barrier cannot move above it.
-  __shared__ uint32_t zero_word;
-  if (tid == 0) zero_word = static_cast<uint32_t>(K) >> 31;
+  // Three register sets in a ring, two LDS buffers.  Half-step i (stage
+  // s + i): issue the loads of stage s + i + 3 into set i % 3 (stored into
+  // LDS one half-step earlier), compute from LDS buffer i % 2, then store set
+  // (i + 1) % 3 -- stage s + i + 1, loaded two half-steps ago -- into buffer
+  // (i + 1) % 2.  Every index is a compile-time constant in the unrolled
+  // loop, so no register set is ever copied and the vmcnt waits stay exact.
+  StageRegs rs[3];
+#define Q4_HALF(I)                                          \
+  do {                                                      \
+    load(s + (I) + 3, rs[(I) % 3]);                         \
+    __builtin_amdgcn_sched_barrier(0);                      \
+    compute((I) % 2);                                       \
+    store(rs[((I) + 1) % 3], ((I) + 1) % 2);                \
+    __syncthreads();                                        \
+  } while (0)
 
-  StageRegs r0, r1;
-  load(0, r0);
-  load(1, r1);
-  __syncthreads();  // zero_word is visible
-  store(r0, 0, 0u);
+  load(0, rs[0]);
+  load(1, rs[1]);
+  load(2, rs[2]);
+  store(rs[0], 0);
   __syncthreads();
-  uint32_t z = zero_word;
-  // Entering with s even: LDS buf 0 holds stage s, r1 holds stage s+1.  Each
-  // half-step issues the loads two stages ahead, computes one stage and
-  // stores the next; one exit keeps the accumulators in place.
   int s = 0;
-  for (; s + 1 < nbp; s += 2) {
-    load(s + 2, r0);
-    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the compute
-    compute(0);
-    store(r1, 1, z);
-    __syncthreads();
-    z = zero_word;
-    load(s + 3, r1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    store(r0, 0, z);
-    __syncthreads();
-    z = zero_word;
+  for (; s + 6 <= nbp; s += 6) {
+    Q4_HALF(0); Q4_HALF(1); Q4_HALF(2); Q4_HALF(3); Q4_HALF(4); Q4_HALF(5);
   }
-  if (s < nbp) compute(0);  // odd number of stages: the last one is in buf 0
+  // remaining stages (uniform branches; at most five half-steps)
+  const int rem = nbp - s;
+  if (rem > 0) Q4_HALF(0);
+  if (rem > 1) Q4_HALF(1);
+  if (rem > 2) Q4_HALF(2);
+  if (rem > 3) Q4_HALF(3);
+  if (rem > 4) Q4_HALF(4);
+#undef Q4_HALF
 
   // 16 x 16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + v.
 #pragma unroll
@@ -224,8 +241,8 @@ __global__ __launch_bounds__(T_THREADS) void matmul_tile_kernel(
       if (row >= M) continue;
       float* yr = Y + static_cast<int64_t>(row) * N;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
         if (col < N) yr[col] = acc[i][j][v];
       }
     }

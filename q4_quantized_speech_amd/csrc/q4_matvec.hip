@@ -23,8 +23,8 @@
 //  * workgroups are persistent (a grid-stride loop over row groups).
 // The argmax variant (the LM head over the 131072-row table that section
 // "Solutions techniques", item 3, keeps in Q4) tracks the best (value, lowest
-// index) per lane, reduces it per workgroup, and the last workgroup to finish
-// folds the per-workgroup partials in a fixed order.
+// index) per lane and reduces it per workgroup into a workspace slot; a small
+// second kernel folds the slots in a fixed order.
 
 #include "q4_device.h"
 #include "q4_kernels.h"
@@ -70,29 +70,28 @@ __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
   }
 }
 
-// Workspace layout: counters [64] uint32 (256 B), then partials
-// [M][AM_MAX_PARTIALS] of uint64 {low: float bits of the value, high: index}.
-__device__ __forceinline__ void am_finish(float bv, int bi, int m, int32_t* out_idx, float* out_val,
-                                          void* workspace) {
-  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
-  uint64_t* partials = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(workspace) + 256) +
-                       static_cast<int64_t>(m) * AM_MAX_PARTIALS;
-  __shared__ int s_last;
+// Workspace layout: partials [M][AM_MAX_PARTIALS] of uint64
+// {low: float bits of the value, high: index}.  Each workgroup writes its own
+// slot; a second kernel folds them (kernel boundaries order the writes, so no
+// fences or counters are needed and the workspace needs no initial value).
+__device__ __forceinline__ void am_write_partial(float bv, int bi, int m, void* workspace) {
+  uint64_t* partials = reinterpret_cast<uint64_t*>(workspace) + static_cast<int64_t>(m) * AM_MAX_PARTIALS;
   am_block_reduce(bv, bi);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0)
     partials[blockIdx.x] = static_cast<uint64_t>(__float_as_uint(bv)) |
                            (static_cast<uint64_t>(static_cast<uint32_t>(bi)) << 32);
-    __threadfence();
-    const unsigned t = atomicAdd(&counters[m], 1u);
-    s_last = (t == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
+
+// One workgroup per row of x: fold the partials in a fixed order.
+__global__ __launch_bounds__(256) void argmax_fold_kernel(const void* workspace, int nparts,
+                                                          int32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_val) {
+  const int m = blockIdx.x;
+  const uint64_t* partials = reinterpret_cast<const uint64_t*>(workspace) + static_cast<int64_t>(m) * AM_MAX_PARTIALS;
   float v = 0.f;
   int i = -1;
-  for (int p = threadIdx.x; p < static_cast<int>(gridDim.x); p += blockDim.x) {
-    const uint64_t e = __builtin_nontemporal_load(&partials[p]);
+  for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
+    const uint64_t e = partials[p];
     const float ev = __uint_as_float(static_cast<uint32_t>(e));
     const int ei = static_cast<int>(static_cast<uint32_t>(e >> 32));
     if (am_better(ev, ei, v, i)) { v = ev; i = ei; }
@@ -101,7 +100,6 @@ __device__ __forceinline__ void am_finish(float bv, int bi, int m, int32_t* out_
   if (threadIdx.x == 0) {
     out_idx[m] = i;
     if (out_val) out_val[m] = i >= 0 ? v : __builtin_nanf("");
-    counters[m] = 0u;  // leave the workspace zero for the next call
   }
 }
 
@@ -241,7 +239,7 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
       row0 = r2;
     }
   }
-  if constexpr (ARGMAX) am_finish(bv, bi, m, out_idx, out_val, workspace);
+  if constexpr (ARGMAX) am_write_partial(bv, bi, m, workspace);
 }
 
 // Generic kernel: any K % 32 == 0 (odd block counts, very long rows).  16
@@ -285,12 +283,13 @@ __global__ __launch_bounds__(256) void matvec_any_kernel(
       if (ok && j == 0) Y[static_cast<int64_t>(m) * N + row] = v;
     }
   }
-  if constexpr (ARGMAX) am_finish(bv, bi, m, out_idx, out_val, workspace);
+  if constexpr (ARGMAX) am_write_partial(bv, bi, m, workspace);
 }
 
+// Returns the number of workgroups per row of x (argmax partials).
 template <int KS, bool ARGMAX>
-void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
-                  int64_t M, int64_t N, int64_t K, hipStream_t s) {
+int64_t launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
+                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const int64_t rows = 4 * MV_R;
   const int64_t passes = (N + rows - 1) / rows;
   // A persistent grid must not exceed what is resident at once: a second,
@@ -308,6 +307,7 @@ void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, floa
   if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
   hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX>), dim3(static_cast<unsigned>(g), M),
                      dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
+  return g;
 }
 
 template <bool ARGMAX>
@@ -315,21 +315,28 @@ hipError_t launch_mv(const uint8_t* w, const float* x, float* y, int32_t* idx, f
                      void* ws, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   // more than 12 waves per workgroup would cap registers below the lane's x slice
   const int64_t ks = (K % 64 == 0 && K <= 12288) ? (K / 64 + 15) / 16 : 0;
+  int64_t g = 0;
   switch (ks) {
 #define Q4_MV_CASE(n) \
-  case n: launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
+  case n: g = launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
     Q4_MV_CASE(1) Q4_MV_CASE(2) Q4_MV_CASE(3) Q4_MV_CASE(4) Q4_MV_CASE(5) Q4_MV_CASE(6)
     Q4_MV_CASE(7) Q4_MV_CASE(8) Q4_MV_CASE(9) Q4_MV_CASE(10) Q4_MV_CASE(11) Q4_MV_CASE(12)
 #undef Q4_MV_CASE
     default: {
       const int cu = device_info().cu_count;
-      int64_t g = (N + 15) / 16;
+      g = (N + 15) / 16;
       const int64_t cap = static_cast<int64_t>(cu) * 8;
       if (g > cap) g = cap;
       if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
       hipLaunchKernelGGL((matvec_any_kernel<ARGMAX>), dim3(static_cast<unsigned>(g), M), dim3(256),
                          0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
     }
+  }
+  if (ARGMAX) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(argmax_fold_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, ws,
+                       static_cast<int>(g), idx, val);
   }
   return hipGetLastError();
 }
@@ -342,7 +349,7 @@ hipError_t launch_matvec(const uint8_t* w, const float* x, float* y, int64_t M, 
 }
 
 size_t lmhead_workspace_bytes(int64_t M) {
-  return 256 + static_cast<size_t>(M) * AM_MAX_PARTIALS * 8;
+  return static_cast<size_t>(M) * AM_MAX_PARTIALS * 8;
 }
 
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,

@@ -270,6 +270,7 @@ def test_lmhead_workspace_reuse_and_odd_k():
     n, k = 700, 96
     qb = O.quantize_q4_0(_rand_w(n, k, 5))
     ws = q4.lmhead_workspace(1, "cuda")
+    ws.fill_(0xA5)                                # any initial contents
     wq = dev(qb)
     for s in range(4):
         x = _rand_x(1, k, 300 + s)
@@ -277,8 +278,6 @@ def test_lmhead_workspace_reuse_and_odd_k():
         idx, _ = q4.lmhead_argmax(wq, dev(x), workspace=ws)
         y, b = O.lmhead_logits(qb, x[0], n, k)
         assert O.argmax_accepts(y, b, int(host(idx)[0]))
-    assert int(host(ws).astype(np.int64).sum()) >= 0
-    assert np.all(host(ws)[:256] == 0)            # counters back to zero
 
 
 def test_lmhead_full_table():

@@ -256,14 +256,15 @@ def main():
             wc = [w] + [w.clone() for _ in range(r - 1)]
             x = torch.from_numpy(synth.activations(m, k, synth.seed_for(seed_cfg, 10 + t))).cuda()
             y = torch.empty((m, n), device="cuda")
-            us = timed(lambda i: q4.matmul(wc[i % r], x, out=y, stream=stream), r)
+            ws = q4.matmul_workspace(m, n, k, "cuda")
+            us = timed(lambda i: q4.matmul(wc[i % r], x, out=y, workspace=ws, stream=stream), r)
             flop = 2.0 * m * n * k
             out[f"{name}_M{m}_{n}x{k}"] = {
                 "us": round(us, 3), "tflops": round(flop / (us * 1e-6) / 1e12, 2),
                 "weight_gbs": round(weight_bytes(n, k) / (us * 1e-6) / 1e9, 1)}
             tot_flop += flop
             tot_us += us
-            del wc, w, x, y
+            del wc, w, x, y, ws
         return out, tot_flop, tot_us
 
     enc_shapes = list(synth.ENCODER_LAYER) + [synth.ADAPTER]

@@ -90,13 +90,26 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  * width 1280, the 4x-downsample adapter, the decoder's 38/76-token prefix of
  * section "Correction du padding Q4"): Y = X * deq(W)^T.
  *   w_q4 : N rows of Q4_0.  x : [M, K] float32.  y : [M, N] float32.
- *   1 <= M <= 65535*128, 1 <= N < 2^31, K a positive multiple of 32.
+ *   1 <= M <= 65535*128, 1 <= N < 2^31, K a positive multiple of 32 and at
+ *   most 4194304.
+ *   workspace, ws_bytes : optional device scratch (NULL allowed).  When the
+ *             output tiles alone cannot fill the GPU, K is split over
+ *             several workgroups whose float32 partial sums go to the
+ *             workspace and are added in a fixed order by a second launch;
+ *             q4_matmul_workspace_bytes(M, N, K) is the size that allows the
+ *             planned split on the current device (0: no split planned).  A
+ *             smaller workspace gives fewer splits (never an error).  Calls
+ *             that share a workspace must be ordered.
  * Weights and activations are rounded to binary16 (round to nearest even) and
  * multiplied on the matrix cores with float32 accumulation, so |x| must stay
- * below 65504.  Deterministic.
+ * below 65504.  Deterministic for a given shape, device and ws_bytes; the
+ * split changes the order of the float32 sums, so results for different
+ * workspace sizes may differ by rounding.
  */
+size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 q4_status q4_matmul(const void* w_q4, const float* x, float* y,
-                    int64_t M, int64_t N, int64_t K, void* stream);
+                    int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * q4_embed_rows -- token-embedding lookup (section "Solutions techniques pour

@@ -7,7 +7,7 @@ fallback: if the library is not built, every entry point raises.
 
 Entry points (same names as the C ABI, minus the ``q4_`` prefix):
     matvec(w_q4, x, out=None)                    y = deq(W) x          (M <= 8)
-    matmul(w_q4, x, out=None)                    Y = X deq(W)^T        (matrix cores)
+    matmul(w_q4, x, out=None, workspace=True)    Y = X deq(W)^T        (matrix cores)
     embed_rows(table_q4, ids, out=None)          rows of deq(T)
     lmhead_argmax(w_q4, x, workspace=None, ...)  argmax_n (deq(T) x)_n
     quantize(w, out=None, check=True)            float32 -> Q4_0 bytes
@@ -54,7 +54,8 @@ _SIGS = {
     "q4_last_hip_error": ([], ctypes.c_int),
     "q4_row_bytes": ([_I64], _SZ),
     "q4_matvec": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
-    "q4_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "q4_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q4_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_embed_rows": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
@@ -141,15 +142,33 @@ def matvec(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     return out.view(n) if squeeze else out
 
 
-def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
-    """Y = X deq(W)^T on the matrix cores (binary16 operands, float32 accumulation)."""
+def matmul_workspace(m: int, n: int, k: int, device) -> torch.Tensor | None:
+    """A workspace for matmul's K split on the current device (None if no split is planned)."""
+    nbytes = int(lib().q4_matmul_workspace_bytes(m, n, k))
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None | bool = True, stream=None):
+    """Y = X deq(W)^T on the matrix cores (binary16 operands, float32 accumulation).
+
+    ``workspace``: a uint8 device tensor for the K split, ``True`` to allocate the
+    planned size here, or ``None``/``False`` for no split."""
     n, k = q4_shape(w_q4)
     x2 = _as_2d_f32(x, k)
     m = x2.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _need_cuda(w_q4, x2, out)
-    _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _stream(stream)), "q4_matmul")
+    if workspace is True:
+        workspace = matmul_workspace(m, n, k, x.device)
+    elif workspace is False:
+        workspace = None
+    _need_cuda(w_q4, x2, out, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _ptr(workspace), ws_bytes,
+                           _stream(stream)), "q4_matmul")
     return out
 
 

@@ -23,6 +23,12 @@ q4_status hip_status(hipError_t e) {
 }
 
 bool k_ok(int64_t K) { return K > 0 && K % 32 == 0 && K <= (int64_t(1) << 30); }
+
+bool matmul_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= int64_t(65535) * 128 && N >= 1 && N < (int64_t(1) << 31) && k_ok(K) &&
+         K <= (int64_t(1) << 22) && N * K < (int64_t(1) << 40) && M * K < (int64_t(1) << 40) &&
+         M * N < (int64_t(1) << 40);
+}
 }  // namespace
 
 DeviceInfo device_info() {
@@ -43,7 +49,7 @@ using namespace q4;
 
 extern "C" {
 
-int q4_abi_version(void) { return 1; }
+int q4_abi_version(void) { return 2; }
 
 const char* q4_status_string(q4_status status) {
   switch (status) {
@@ -74,14 +80,19 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y, int64_t M, int64
                                   static_cast<hipStream_t>(stream)));
 }
 
+size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!matmul_shape_ok(M, N, K)) return 0;
+  return matmul_workspace_bytes(M, N, K, device_info().cu_count);
+}
+
 q4_status q4_matmul(const void* w_q4, const float* x, float* y, int64_t M, int64_t N, int64_t K,
-                    void* stream) {
+                    void* workspace, size_t ws_bytes, void* stream) {
   if (!w_q4 || !x || !y) return Q4_ERR_NULL;
-  if (M < 1 || M > int64_t(65535) * 128 || N < 1 || N >= (int64_t(1) << 31) || !k_ok(K) ||
-      N * K >= (int64_t(1) << 40) || M * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40))
-    return Q4_ERR_SHAPE;
-  if (!aligned16(w_q4) || !aligned16(x) || !aligned16(y)) return Q4_ERR_ALIGN;
-  return hip_status(launch_matmul(static_cast<const uint8_t*>(w_q4), x, y, M, N, K,
+  if (!matmul_shape_ok(M, N, K)) return Q4_ERR_SHAPE;
+  if (!aligned16(w_q4) || !aligned16(x) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    return Q4_ERR_ALIGN;
+  return hip_status(launch_matmul(static_cast<const uint8_t*>(w_q4), x, y, M, N, K, workspace,
+                                  workspace ? ws_bytes : 0, device_info().cu_count,
                                   static_cast<hipStream_t>(stream)));
 }
 

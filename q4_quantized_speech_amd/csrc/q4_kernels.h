@@ -20,7 +20,8 @@ hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_i
 size_t lmhead_workspace_bytes(int64_t M);
 
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
-                         int64_t K, hipStream_t s);
+                         int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s);
+size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
 
 hipError_t launch_embed(const uint8_t* table, const int32_t* ids, float* out, int64_t M,
                         int64_t N, int64_t K, hipStream_t s);

@@ -17,17 +17,23 @@
 //
 // Main kernel (K % 64 == 0): a 256-thread workgroup owns a 128 x 128 tile of
 // Y; each of its four waves a 64 x 64 sub-tile (4 x 4 MFMA tiles).  K
-// advances in stages of 64 (one 36-byte block pair per weight row).  Per
-// stage the workgroup converts X and decodes W once into LDS (double
-// buffered, in operand order, so fragments are contiguous 1 KiB LDS rows),
-// while the global loads of the next three stages are in flight in a ring of
-// three register sets (fixed roles in an unrolled loop: no register copies,
-// so the in-order vmcnt counter stays exact).  64 KiB of LDS per workgroup
-// lets two workgroups share a CU.  Tiles are renumbered so each XCD
-// (8 per chip, each with its own L2) works on a contiguous range of tiles that
-// share rows of X.
+// advances in stages of 64 (one 36-byte block pair per weight row).  Global
+// loads are coalesced (16 lanes read one row of X; consecutive lanes read
+// consecutive dwords of the stage's weight bytes) and go through range-checked
+// buffer resources, so rows past M or N read as zeros.  Per stage the
+// workgroup converts X to binary16 and decodes W (from raw codes staged in LDS
+// one stage earlier) into LDS in operand order, double buffered, while the
+// loads of later stages are in flight in a ring of three register sets.  73
+// KiB of LDS per workgroup lets two workgroups share a CU.  When the tiles
+// cannot fill the GPU, K is split over several workgroups per tile; their
+// partial tiles go to a workspace and a second kernel adds them in a fixed
+// order.  Tiles are renumbered so each XCD (8 per chip, each with its own L2)
+// works on a contiguous range of tiles that share rows of X.
 //
 // A simple kernel (128 x 128 tiles, one block per stage) covers K % 64 == 32.
+
+#include <algorithm>
+#include <cstdint>
 
 #include "q4_device.h"
 #include "q4_kernels.h"
@@ -86,61 +92,104 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: 128 x 128 tiles, K % 64 == 0.
+// Main kernel: 128 x 128 tiles, K % 64 == 0, K optionally split over several
+// workgroups per tile.
 // ---------------------------------------------------------------------------
 constexpr int T_BM = 128, T_BN = 128, T_THREADS = 256;
+constexpr int WRAW_DW = T_BN * PAIR_BYTES / 4;  // raw code dwords of one stage: 1152
+constexpr int MAX_SPLITS = 16;
+constexpr int W_LANES = 28 * 9;                      // lanes of a 28-row code load
+constexpr int W_LAST_LANES = (T_BN - 4 * 28) * 9;    // the last 16 rows
+static_assert(4 * W_LANES + W_LAST_LANES == WRAW_DW, "code loads cover the stage");
 
-// Stage registers of one thread.  Roles are wave-uniform: waves 0-1 stage
-// block 0 of the pair, waves 2-3 block 1; thread t stages row t % 128 of X
-// and of W for that block.
-struct StageRegs {
-  f32x4 a[8];     // X: the 32 floats of the block
-  uint32_t b[5];  // W: the 20 bytes starting at 16 * block within the pair
-};
+// Raw buffer resource over [base, base + bytes): 32-bit data, range checked,
+// so loads past the end return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
 
-// Two waves per SIMD is the occupancy target (two workgroups per CU, 64 KiB
-// of LDS each); saying so keeps all accumulators in VGPRs.
+struct XRegs { f32x4 a[8]; };     // chunk j of rows r + 16 u, u < 8
+struct WRegs { uint32_t b[5]; };  // code dwords of rows 28 u + t / 9, u < 5
+
+// Loader roles (thread t of 256).
+//  X: j = t % 16 is a 16-byte chunk of a row's 256-byte stage span, r = t / 16
+//     a row; rows r + 16 u.  Sixteen lanes read one row's span, so one load
+//     instruction covers four whole rows (a lane per row would touch 64 cache
+//     lines per instruction and saturate the address unit).  Chunk j holds
+//     k = 4 j .. 4 j + 3: block j / 8, slot g = j % 4, low half (k 4g..4g+3)
+//     if j % 8 < 4, else high half (k 16+4g..16+4g+3).
+//  W: the stage's 128 rows x 36 bytes are 1152 dwords, loaded in five rounds
+//     of up to 252 lanes (28 rows x 9 dwords): consecutive lanes read
+//     consecutive dwords of a row.  They go to LDS as they are (row-major,
+//     9 dwords a row) and are decoded one stage later by thread
+//     (row t % 128, block t / 128).
+// LDS: X in operand order, swizzled so that both the 8-byte writes of a row's
+// 16 lanes and the 16-byte operand reads hit distinct banks: slot g of row
+// r (block b) sits at element 16 g + (r % 16 ^ (g + 4 b)) of its 16-row tile.
 __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
-                        float* __restrict__ Y, int M, int N, int K, int tiles_n, int ntiles) {
-  // [buf][block of the pair][16-row tile][lane]: 2 x 32 KiB
-  __shared__ f16x8 As[2][2][T_BM / 16][64];
+                        float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
+                        int tiles_n, int ntiles, int split_stages) {
+  __shared__ f16x8 As[2][2][T_BM / 16][64];  // [buf][block][16-row tile][element]
   __shared__ f16x8 Bs[2][2][T_BN / 16][64];
+  __shared__ uint32_t Wraw[2][WRAW_DW];
 
-  const int tile = xcd_tile(blockIdx.x, ntiles);
+  const int item = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = item / ntiles, tile = item % ntiles;
   const int m0 = (tile / tiles_n) * T_BM;
   const int n0 = (tile % tiles_n) * T_BN;
-  const int nbp = K >> 6;  // stages
+  const int nbp = K >> 6;
+  const int s0 = split * split_stages;
+  const int nst = min(nbp - s0, split_stages);  // >= 1 (host guarantees)
   const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loader roles.  Rows past M and columns past N are clamped to the last
-  // valid one: they only feed outputs that are never stored, so no masking
-  // (a mask on loaded data would pull a wait for this stage's loads forward).
-  const int lr = tid & 127, blk = tid >> 7;  // row within the tile, block of the pair
-  const int am = m0 + lr;
-  const float* xrow = X + static_cast<int64_t>(am < M ? am : M - 1) * K + 32 * blk;
-  const int bn = n0 + lr;
-  const uint8_t* wrow = W + static_cast<int64_t>(bn < N ? bn : N - 1) * rb + 16 * blk;
-
-  auto load = [&](int s, StageRegs& r) {
-    s = s < nbp ? s : nbp - 1;  // past the end: reload the last stage (unused)
-    const f32x4* xp = reinterpret_cast<const f32x4*>(xrow + 64 * s);
+  // X: one resource per group of 16 rows, so rows past M read as zeros.
+  const int xj = tid & 15, xr = tid >> 4;
+  __amdgpu_buffer_rsrc_t xrs[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r.a[u] = xp[u];
-    const uint8_t* wp = wrow + static_cast<int64_t>(s) * PAIR_BYTES;
-    const u32x4a p0 = *reinterpret_cast<const u32x4a*>(wp);
-    r.b[0] = p0.x; r.b[1] = p0.y; r.b[2] = p0.z; r.b[3] = p0.w;
-    r.b[4] = *reinterpret_cast<const uint32_t*>(wp + 16);
+  for (int u = 0; u < 8; ++u)
+    xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + 16 * u) * K,
+                       static_cast<int64_t>(M - m0 - 16 * u) * K * 4);
+  const int xvo = xr * K * 4 + xj * 16;
+  const int xb = xj >> 3, xh = (xj >> 2) & 1, xg = xj & 3;
+  const int xe = 16 * xg + (xr ^ (xg + 4 * xb));
+
+  // W: load u covers rows 28 u .. 28 u + 27 (u < 4) or 112 .. 127 (u = 4),
+  // lane t dword t % 9 of row 28 u + t / 9; one resource per group of rows,
+  // so rows past N read as zeros (scale 0: they decode to zeros).
+  __amdgpu_buffer_rsrc_t wrs[5];
+#pragma unroll
+  for (int u = 0; u < 5; ++u)
+    wrs[u] = make_rsrc(W + static_cast<int64_t>(n0 + 28 * u) * rb,
+                       static_cast<int64_t>(N - n0 - 28 * u) * rb);
+  const int wq = tid / 9;
+  const int wvo = static_cast<int>(wq * rb) + (tid - 9 * wq) * 4;
+  const bool wlane = tid < W_LANES, wlast = tid < W_LAST_LANES;
+  const int lr = tid & 127, blk = tid >> 7;  // decode role: row, block of the pair
+
+  auto load_x = [&](int t, XRegs& r) {
+    const int so = (s0 + (t < nst ? t : nst - 1)) * 256;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      r.a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, so, 0));
+  };
+  auto load_w = [&](int t, WRegs& r) {
+    const int so = (s0 + (t < nst ? t : nst - 1)) * PAIR_BYTES;
+    if (wlane) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r.b[u] = __builtin_amdgcn_raw_buffer_load_b32(wrs[u], wvo, so, 0);
+    }
+    if (wlast) r.b[4] = __builtin_amdgcn_raw_buffer_load_b32(wrs[4], wvo, so, 0);
   };
 
-  // Ordering guard.  The conversion of a register set is pure arithmetic, so
-  // the compiler would hoist it above the barrier to right behind that set's
-  // loads, making the wave wait for loads it has just issued.  The first
-  // operation on every loaded register is therefore a volatile asm VALU op
-  // (the binary16 pack for X, a move for W): volatile asm keeps its place
-  // after the barrier, and everything else depends on it.
+  // Ordering guard.  Conversions of loaded registers are pure arithmetic, so
+  // the compiler would hoist them to right behind their loads, making the
+  // wave wait for loads it has just issued.  The first operation on every
+  // loaded register is a volatile asm op (the binary16 pack for X, a move for
+  // W), which keeps its place in the program; everything else depends on it.
   auto pk_f16 = [](float a, float b) -> uint32_t {
     uint32_t r;
     asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -152,23 +201,34 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
     return r;
   };
 
-  auto store = [&](const StageRegs& r, int buf) {
-    // X: lane slot (row % 16) + 16 g holds k {4g..4g+3, 16+4g..16+4g+3}
+  auto store_x = [&](const XRegs& r, int buf) {
+    char* base = reinterpret_cast<char*>(&As[buf][xb][0][xe]) + 8 * xh;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lo = r.a[g], hi = r.a[4 + g];
-      const u32x4a h = {pk_f16(lo.x, lo.y), pk_f16(lo.z, lo.w), pk_f16(hi.x, hi.y), pk_f16(hi.z, hi.w)};
-      *reinterpret_cast<u32x4a*>(&As[buf][blk][lr >> 4][(lr & 15) + 16 * g]) = h;
+    for (int u = 0; u < 8; ++u) {
+      const f32x4 v = r.a[u];
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
+      *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
     }
+  };
+  auto store_w = [&](const WRegs& r, int buf) {
+    if (wlane) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Wraw[buf][W_LANES * u + tid] = pin(r.b[u]);
+    }
+    if (wlast) Wraw[buf][4 * W_LANES + tid] = pin(r.b[4]);
+  };
+  auto decode = [&](int buf) {
+    const uint32_t* wr = &Wraw[buf][lr * 9 + blk * 4];
     uint32_t b[5];
 #pragma unroll
-    for (int t = 0; t < 5; ++t) b[t] = pin(r.b[t]);
-    if (blk == 0) {  // wave-uniform: bytes 0..19 = scale, codes at byte 2
+    for (int t = 0; t < 5; ++t) b[t] = wr[t];
+    if (blk == 0) {  // wave-uniform: bytes 0..19 = scale, codes from byte 2
       const uint32_t d = b[0] & 0xFFFFu;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         Bs[buf][0][lr >> 4][(lr & 15) + 16 * g] = decode8_f16(shift16(b[g + 1], b[g]), d);
-    } else {         // bytes 16..35 = (2 bytes of block 0), scale, codes at byte 4
+    } else {         // bytes 16..35 = 2 bytes of block 0, scale, codes from byte 20
       const uint32_t d = b[0] >> 16;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -182,12 +242,17 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
+  // operand element of this lane in each block (swizzled X, plain W)
+  const int ag = lane >> 4;
+  const int ae0 = 16 * ag + ((lane & 15) ^ ag);
+  const int ae1 = 16 * ag + ((lane & 15) ^ (ag + 4));
   auto compute = [&](int buf) {
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
       f16x8 a[4], b[4];
+      const int ae = bk ? ae1 : ae0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[buf][bk][wm * 4 + i][lane];
+      for (int i = 0; i < 4; ++i) a[i] = As[buf][bk][wm * 4 + i][ae];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = Bs[buf][bk][wn * 4 + j][lane];
 #pragma unroll
@@ -198,53 +263,89 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
     }
   };
 
-  // Three register sets in a ring, two LDS buffers.  Half-step i (stage
-  // s + i): issue the loads of stage s + i + 3 into set i % 3 (stored into
-  // LDS one half-step earlier), compute from LDS buffer i % 2, then store set
-  // (i + 1) % 3 -- stage s + i + 1, loaded two half-steps ago -- into buffer
-  // (i + 1) % 2.  Every index is a compile-time constant in the unrolled
-  // loop, so no register set is ever copied and the vmcnt waits stay exact.
-  StageRegs rs[3];
-#define Q4_HALF(I)                                          \
+  // Pipeline over the stages t of this split (buffers and register sets are
+  // indexed by t, all compile-time constants in the unrolled loop).  Step t:
+  // issue the loads of X(t + 3) and W(t + 4); multiply stage t from LDS
+  // buffer t % 2; decode the raw codes of stage t + 1 into buffer (t + 1) % 2;
+  // convert X(t + 1) into buffer (t + 1) % 2; put the raw codes of stage t + 2
+  // into raw buffer t % 2; barrier.  Loads have two steps to arrive.
+  XRegs rx[3];
+  WRegs rw[3];
+#define Q4_STEP(I)                                          \
   do {                                                      \
-    load(s + (I) + 3, rs[(I) % 3]);                         \
+    load_x(t + (I) + 3, rx[(I) % 3]);                       \
+    load_w(t + (I) + 4, rw[(I) % 3]);                       \
     __builtin_amdgcn_sched_barrier(0);                      \
     compute((I) % 2);                                       \
-    store(rs[((I) + 1) % 3], ((I) + 1) % 2);                \
+    decode(((I) + 1) % 2);                                  \
+    store_x(rx[((I) + 1) % 3], ((I) + 1) % 2);              \
+    store_w(rw[((I) + 1) % 3], (I) % 2);                    \
     __syncthreads();                                        \
   } while (0)
 
-  load(0, rs[0]);
-  load(1, rs[1]);
-  load(2, rs[2]);
-  store(rs[0], 0);
+  load_x(0, rx[0]);
+  load_w(0, rw[0]);
+  load_w(1, rw[1]);
+  store_w(rw[0], 0);
+  store_w(rw[1], 1);
+  store_x(rx[0], 0);
+  load_x(1, rx[1]);
+  load_w(2, rw[1]);
+  load_x(2, rx[2]);
+  load_w(3, rw[2]);
   __syncthreads();
-  int s = 0;
-  for (; s + 6 <= nbp; s += 6) {
-    Q4_HALF(0); Q4_HALF(1); Q4_HALF(2); Q4_HALF(3); Q4_HALF(4); Q4_HALF(5);
+  decode(0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 6 <= nst; t += 6) {
+    Q4_STEP(0); Q4_STEP(1); Q4_STEP(2); Q4_STEP(3); Q4_STEP(4); Q4_STEP(5);
   }
-  // remaining stages (uniform branches; at most five half-steps)
-  const int rem = nbp - s;
-  if (rem > 0) Q4_HALF(0);
-  if (rem > 1) Q4_HALF(1);
-  if (rem > 2) Q4_HALF(2);
-  if (rem > 3) Q4_HALF(3);
-  if (rem > 4) Q4_HALF(4);
-#undef Q4_HALF
+  const int rem = nst - t;  // uniform; at most five more steps
+  if (rem > 0) Q4_STEP(0);
+  if (rem > 1) Q4_STEP(1);
+  if (rem > 2) Q4_STEP(2);
+  if (rem > 3) Q4_STEP(3);
+  if (rem > 4) Q4_STEP(4);
+#undef Q4_STEP
 
   // 16 x 16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + v.
+  // With a split, partial sums go to slice `split` of P ([splits][M][N]).
+  float* out = P ? P + static_cast<int64_t>(split) * M * N : Y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + v;
       if (row >= M) continue;
-      float* yr = Y + static_cast<int64_t>(row) * N;
+      float* yr = out + static_cast<int64_t>(row) * N;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + j * 16 + (lane & 15);
         if (col < N) yr[col] = acc[i][j][v];
       }
+    }
+  }
+}
+
+// Y = sum over s of P[s] in the order s = 0, 1, ... (deterministic).
+__global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restrict__ P,
+                                                          float* __restrict__ Y, int64_t mn,
+                                                          int splits) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  if ((mn & 3) == 0) {
+    const int64_t n4 = mn >> 2;
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(P);
+    f32x4* y4 = reinterpret_cast<f32x4*>(Y);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      f32x4 a = p4[i];
+      for (int s = 1; s < splits; ++s) a += p4[i + s * n4];
+      y4[i] = a;
+    }
+  } else {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < mn; i += stride) {
+      float a = P[i];
+      for (int s = 1; s < splits; ++s) a += P[i + s * mn];
+      Y[i] = a;
     }
   }
 }
@@ -352,15 +453,51 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 
 }  // namespace
 
+// K-split plan of the main kernel: enough workgroups for two per CU when the
+// tile count alone does not give them, at least 8 stages (512 of K) per
+// split, at most MAX_SPLITS, and never a partial buffer beyond ws_bytes.
+static int plan_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, int* stages) {
+  const int64_t ntiles = ((M + T_BM - 1) / T_BM) * ((N + T_BN - 1) / T_BN);
+  const int nbp = static_cast<int>(K / 64);
+  int64_t want = (2 * static_cast<int64_t>(cus)) / ntiles;
+  want = std::min<int64_t>(want, nbp / 8);
+  want = std::min<int64_t>(want, MAX_SPLITS);
+  const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
+  while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
+  if (want < 2) {
+    *stages = nbp;
+    return 1;
+  }
+  const int per = static_cast<int>((nbp + want - 1) / want);
+  *stages = per;
+  return (nbp + per - 1) / per;  // every split non-empty
+}
+
+size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  if (K % 64 != 0) return 0;
+  int stages = 0;
+  const int splits = plan_splits(M, N, K, cus, SIZE_MAX, &stages);
+  return splits > 1 ? static_cast<size_t>(splits) * M * N * sizeof(float) : 0;
+}
+
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
-                         int64_t K, hipStream_t s) {
+                         int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
   if (K % 64 == 0) {
     const int tiles_n = static_cast<int>((N + T_BN - 1) / T_BN);
     const int tiles_m = static_cast<int>((M + T_BM - 1) / T_BM);
     const int ntiles = tiles_n * tiles_m;
-    hipLaunchKernelGGL(matmul_tile_kernel, dim3(ntiles), dim3(T_THREADS), 0, s, w, x, y,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
-                       ntiles);
+    int stages = 0;
+    const int splits = plan_splits(M, N, K, cus, ws ? ws_bytes : 0, &stages);
+    float* P = splits > 1 ? static_cast<float*>(ws) : nullptr;
+    hipLaunchKernelGGL(matmul_tile_kernel, dim3(ntiles * splits), dim3(T_THREADS), 0, s, w, x, y,
+                       P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
+                       ntiles, stages);
+    if (splits > 1) {
+      const int64_t mn = M * N;
+      const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
+      const int blocks = static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
+      hipLaunchKernelGGL(splitk_fold_kernel, dim3(blocks), dim3(256), 0, s, P, y, mn, splits);
+    }
   } else {
     const dim3 grid(static_cast<unsigned>((N + S_BN - 1) / S_BN),
                     static_cast<unsigned>((M + S_BM - 1) / S_BM));

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
 
 def test_basic_queries():
     lib = q4.lib()
-    assert lib.q4_abi_version() == 1
+    assert lib.q4_abi_version() == 2
     assert lib.q4_row_bytes(3072) == 1728
     assert lib.q4_row_bytes(32) == 18
     assert lib.q4_row_bytes(48) == 0
@@ -37,9 +37,13 @@ def test_basic_queries():
     assert lib.q4_lmhead_argmax_workspace_bytes(65, 131072, 3072) == 0
 
 
+def _matmul_no_ws(*args):
+    return q4.lib().q4_matmul(*args[:6], None, 0, args[6])
+
+
 @pytest.mark.parametrize("fn", ["q4_matvec", "q4_matmul", "q4_embed_rows"])
 def test_null_shape_align(fn):
-    f = getattr(q4.lib(), fn)
+    f = _matmul_no_ws if fn == "q4_matmul" else getattr(q4.lib(), fn)
     assert f(None, A, A, 1, 16, 64, None) == q4.Q4_ERR_NULL
     assert f(A, None, A, 1, 16, 64, None) == q4.Q4_ERR_NULL
     assert f(A, A, None, 1, 16, 64, None) == q4.Q4_ERR_NULL
@@ -51,6 +55,21 @@ def test_null_shape_align(fn):
     assert f(A + 4, A, A, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
     assert f(A, A + 8, A, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
     assert f(A, A, A + 2, 1, 16, 64, None) == q4.Q4_ERR_ALIGN
+
+
+def test_matmul_workspace_validation():
+    lib = q4.lib()
+    f = lib.q4_matmul
+    assert f(A, A, A, 4, 16, 64, A + 8, 1024, None) == q4.Q4_ERR_ALIGN   # workspace alignment
+    assert f(A, A, A, 4, 16, 1 << 23, None, 0, None) == q4.Q4_ERR_SHAPE  # K above 2^22
+    # the split plan: few tiles and a long K ask for a workspace; many tiles do not
+    few = lib.q4_matmul_workspace_bytes(100, 200, 4096)
+    assert few > 0 and few % (100 * 200 * 4) == 0
+    assert lib.q4_matmul_workspace_bytes(1500, 1280, 5120) > 0
+    assert lib.q4_matmul_workspace_bytes(3000, 5120, 1280) == 0
+    assert lib.q4_matmul_workspace_bytes(100, 200, 4096 + 32) == 0    # K % 64 == 32: no split
+    assert lib.q4_matmul_workspace_bytes(0, 200, 4096) == 0
+    assert lib.q4_matmul_workspace_bytes(100, 200, 48) == 0
 
 
 def test_matvec_m_range():

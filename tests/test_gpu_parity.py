@@ -216,6 +216,44 @@ def test_matmul_parity_small(m, n, k):
     assert_within(y, ref, b, *MF, f"matmul {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(100, 200, 4096), (16, 3072, 9216), (129, 130, 1024),
+                                   (1, 64, 640)])
+def test_matmul_split_k(m, n, k):
+    """K split over several workgroups per tile: with the planned workspace, a
+    workspace too small for the full plan, and none; all within tolerance, and
+    repeatable bit for bit for a given workspace size."""
+    qb = O.quantize_q4_0(_rand_w(n, k, 3 * m + n))
+    x = _rand_x(m, k, 11 + m)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    full = q4.matmul_workspace(m, n, k, "cuda")
+    if m * n * k > 1 << 20:
+        assert full is not None, "a split is planned for this shape"
+    small = None if full is None else full[: 2 * m * n * 4]
+    for ws, tag in [(full, "planned"), (small, "two slices"), (None, "none")]:
+        announce(f"matmul split-K {m}x{n}x{k} workspace {tag}")
+        y1 = host(q4.matmul(wq, xd, workspace=ws))
+        assert_within(y1, ref, b, *MF, f"split-K {m}x{n}x{k} {tag}")
+        y2 = host(q4.matmul(wq, xd, workspace=ws))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), tag
+
+
+def test_matmul_split_k_stays_in_bounds():
+    """Partial sums stay inside the workspace, results inside Y."""
+    m, n, k = 70, 150, 2048
+    qb = dev(O.quantize_q4_0(_rand_w(n, k, 8)))
+    x = dev(_rand_x(m, k, 9))
+    need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k))
+    assert need > 0
+    sentinel = -12345.0
+    ws = torch.full((need // 4 + 64,), sentinel, dtype=torch.float32, device="cuda")
+    out = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
+    announce("matmul split-K canary")
+    q4.matmul(qb, x, out=out[: m * n].view(m, n), workspace=ws[: need // 4].view(torch.uint8))
+    assert np.all(host(ws)[need // 4:] == sentinel)
+    assert np.all(host(out)[m * n:] == sentinel)
+
+
 @pytest.mark.parametrize("m", [16, 38, 76])
 def test_matmul_decoder_prefix_full(m):
     """The decoder projection set at the prefix lengths 16 / 38 / 76."""

@@ -92,15 +92,11 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: 128 x 128 tiles, K % 64 == 0, K optionally split over several
-// workgroups per tile.
+// Main kernel: 128 x BN tiles (BN = 128 or 256), K % 64 == 0, K optionally
+// split over several workgroups per tile.
 // ---------------------------------------------------------------------------
-constexpr int T_BM = 128, T_BN = 128, T_THREADS = 256;
-constexpr int WRAW_DW = T_BN * PAIR_BYTES / 4;  // raw code dwords of one stage: 1152
+constexpr int T_BM = 128;
 constexpr int MAX_SPLITS = 16;
-constexpr int W_LANES = 28 * 9;                      // lanes of a 28-row code load
-constexpr int W_LAST_LANES = (T_BN - 4 * 28) * 9;    // the last 16 rows
-static_assert(4 * W_LANES + W_LAST_LANES == WRAW_DW, "code loads cover the stage");
 
 // Raw buffer resource over [base, base + bytes): 32-bit data, range checked,
 // so loads past the end return zeros instead of touching memory.
@@ -109,80 +105,109 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-struct XRegs { f32x4 a[8]; };     // chunk j of rows r + 16 u, u < 8
-struct WRegs { uint32_t b[5]; };  // code dwords of rows 28 u + t / 9, u < 5
+template <int BN>
+struct TileCfg {
+  static constexpr int THREADS = 2 * BN;            // 8 or 4 waves: 2 along M, BN / 64 along N
+  static constexpr int WN = BN / 64;
+  static constexpr int XRS = THREADS / 16;          // rows per X load round
+  static constexpr int XU = T_BM / XRS;             // X load rounds (16-byte chunks per thread)
+  static constexpr int WROWS = THREADS / 9;         // rows per W load round
+  static constexpr int WLANES = 9 * WROWS;
+  static constexpr int WFULL = BN / WROWS;          // full W rounds
+  static constexpr int WLAST = BN - WFULL * WROWS;  // rows of the last round
+  static constexpr int WU = WFULL + (WLAST > 0);
+  static constexpr int WRAW = 9 * BN;               // code dwords of one stage
+  static_assert(WFULL * WLANES + 9 * WLAST == WRAW, "code loads cover the stage");
+  static_assert(XU * XRS == T_BM, "X loads cover the tile");
+};
 
-// Loader roles (thread t of 256).
+template <int BN, int D>
+struct StageRing {
+  f32x4 x[D][TileCfg<BN>::XU];
+  uint32_t w[D][TileCfg<BN>::WU];
+};
+
+// Loader roles (thread t).
 //  X: j = t % 16 is a 16-byte chunk of a row's 256-byte stage span, r = t / 16
-//     a row; rows r + 16 u.  Sixteen lanes read one row's span, so one load
+//     a row; rows r + XRS u.  Sixteen lanes read one row's span, so one load
 //     instruction covers four whole rows (a lane per row would touch 64 cache
 //     lines per instruction and saturate the address unit).  Chunk j holds
 //     k = 4 j .. 4 j + 3: block j / 8, slot g = j % 4, low half (k 4g..4g+3)
 //     if j % 8 < 4, else high half (k 16+4g..16+4g+3).
-//  W: the stage's 128 rows x 36 bytes are 1152 dwords, loaded in five rounds
-//     of up to 252 lanes (28 rows x 9 dwords): consecutive lanes read
-//     consecutive dwords of a row.  They go to LDS as they are (row-major,
-//     9 dwords a row) and are decoded one stage later by thread
-//     (row t % 128, block t / 128).
+//  W: the stage's BN rows x 36 bytes, loaded in rounds of WROWS rows x 9
+//     dwords: consecutive lanes read consecutive dwords of a row.  They go to
+//     LDS as they are (9 dwords a row) and are decoded one stage later by
+//     thread (row t % BN, block t / BN).
 // LDS: X in operand order, swizzled so that both the 8-byte writes of a row's
 // 16 lanes and the 16-byte operand reads hit distinct banks: slot g of row
 // r (block b) sits at element 16 g + (r % 16 ^ (g + 4 b)) of its 16-row tile.
-__global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// One resource per load round makes rows past M or N read as zeros.
+//
+// Pipeline over the stages t of this split (buffers and register sets indexed
+// by t, compile-time constants in the unrolled loop).  Step t: issue the loads
+// of X(t + D) and W(t + D + 1); multiply stage t from LDS buffer t % 2; decode
+// the raw codes of stage t + 1 into buffer (t + 1) % 2; convert X(t + 1) into
+// buffer (t + 1) % 2; put the raw codes of stage t + 2 into raw buffer t % 2;
+// barrier.  Loads have D - 1 steps to arrive.
+template <int BN, int D>
+__global__ __launch_bounds__(TileCfg<BN>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
                         float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
                         int tiles_n, int ntiles, int split_stages) {
+  using C = TileCfg<BN>;
   __shared__ f16x8 As[2][2][T_BM / 16][64];  // [buf][block][16-row tile][element]
-  __shared__ f16x8 Bs[2][2][T_BN / 16][64];
-  __shared__ uint32_t Wraw[2][WRAW_DW];
+  __shared__ f16x8 Bs[2][2][BN / 16][64];
+  __shared__ uint32_t Wraw[2][C::WRAW];
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / ntiles, tile = item % ntiles;
   const int m0 = (tile / tiles_n) * T_BM;
-  const int n0 = (tile % tiles_n) * T_BN;
+  const int n0 = (tile % tiles_n) * BN;
   const int nbp = K >> 6;
   const int s0 = split * split_stages;
   const int nst = min(nbp - s0, split_stages);  // >= 1 (host guarantees)
   const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // X: one resource per group of 16 rows, so rows past M read as zeros.
   const int xj = tid & 15, xr = tid >> 4;
-  __amdgpu_buffer_rsrc_t xrs[8];
+  __amdgpu_buffer_rsrc_t xrs[C::XU];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + 16 * u) * K,
-                       static_cast<int64_t>(M - m0 - 16 * u) * K * 4);
+  for (int u = 0; u < C::XU; ++u)
+    xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + C::XRS * u) * K,
+                       static_cast<int64_t>(M - m0 - C::XRS * u) * K * 4);
   const int xvo = xr * K * 4 + xj * 16;
   const int xb = xj >> 3, xh = (xj >> 2) & 1, xg = xj & 3;
-  const int xe = 16 * xg + (xr ^ (xg + 4 * xb));
+  const int xe = 16 * xg + ((xr & 15) ^ (xg + 4 * xb));
 
-  // W: load u covers rows 28 u .. 28 u + 27 (u < 4) or 112 .. 127 (u = 4),
-  // lane t dword t % 9 of row 28 u + t / 9; one resource per group of rows,
-  // so rows past N read as zeros (scale 0: they decode to zeros).
-  __amdgpu_buffer_rsrc_t wrs[5];
+  __amdgpu_buffer_rsrc_t wrs[C::WU];
 #pragma unroll
-  for (int u = 0; u < 5; ++u)
-    wrs[u] = make_rsrc(W + static_cast<int64_t>(n0 + 28 * u) * rb,
-                       static_cast<int64_t>(N - n0 - 28 * u) * rb);
+  for (int u = 0; u < C::WU; ++u)
+    wrs[u] = make_rsrc(W + static_cast<int64_t>(n0 + C::WROWS * u) * rb,
+                       static_cast<int64_t>(N - n0 - C::WROWS * u) * rb);
   const int wq = tid / 9;
   const int wvo = static_cast<int>(wq * rb) + (tid - 9 * wq) * 4;
-  const bool wlane = tid < W_LANES, wlast = tid < W_LAST_LANES;
-  const int lr = tid & 127, blk = tid >> 7;  // decode role: row, block of the pair
+  const bool wlane = tid < C::WLANES, wlast = tid < 9 * C::WLAST;
+  const int lr = tid % BN, blk = tid / BN;  // decode role: row, block of the pair
 
-  auto load_x = [&](int t, XRegs& r) {
+  StageRing<BN, D> ring;
+  auto load_x = [&](int t, int slot) {
     const int so = (s0 + (t < nst ? t : nst - 1)) * 256;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      r.a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, so, 0));
+    for (int u = 0; u < C::XU; ++u)
+      ring.x[slot][u] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, so, 0));
   };
-  auto load_w = [&](int t, WRegs& r) {
+  auto load_w = [&](int t, int slot) {
     const int so = (s0 + (t < nst ? t : nst - 1)) * PAIR_BYTES;
     if (wlane) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r.b[u] = __builtin_amdgcn_raw_buffer_load_b32(wrs[u], wvo, so, 0);
+      for (int u = 0; u < C::WFULL; ++u)
+        ring.w[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs[u], wvo, so, 0);
     }
-    if (wlast) r.b[4] = __builtin_amdgcn_raw_buffer_load_b32(wrs[4], wvo, so, 0);
+    if constexpr (C::WLAST > 0) {
+      if (wlast) ring.w[slot][C::WFULL] = __builtin_amdgcn_raw_buffer_load_b32(wrs[C::WFULL], wvo, so, 0);
+    }
   };
 
   // Ordering guard.  Conversions of loaded registers are pure arithmetic, so
@@ -201,22 +226,24 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
     return r;
   };
 
-  auto store_x = [&](const XRegs& r, int buf) {
-    char* base = reinterpret_cast<char*>(&As[buf][xb][0][xe]) + 8 * xh;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  auto store_x = [&](int slot, int buf) {
+    char* base = reinterpret_cast<char*>(&As[buf][xb][xr >> 4][xe]) + 8 * xh;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const f32x4 v = r.a[u];
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    for (int u = 0; u < C::XU; ++u) {
+      const f32x4 v = ring.x[slot][u];
       const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
-      *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
+      *reinterpret_cast<u32x2*>(base + u * (C::XRS / 16) * 64 * 16) = h;
     }
   };
-  auto store_w = [&](const WRegs& r, int buf) {
+  auto store_w = [&](int slot, int buf) {
     if (wlane) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) Wraw[buf][W_LANES * u + tid] = pin(r.b[u]);
+      for (int u = 0; u < C::WFULL; ++u) Wraw[buf][C::WLANES * u + tid] = pin(ring.w[slot][u]);
     }
-    if (wlast) Wraw[buf][4 * W_LANES + tid] = pin(r.b[4]);
+    if constexpr (C::WLAST > 0) {
+      if (wlast) Wraw[buf][C::WLANES * C::WFULL + tid] = pin(ring.w[slot][C::WFULL]);
+    }
   };
   auto decode = [&](int buf) {
     const uint32_t* wr = &Wraw[buf][lr * 9 + blk * 4];
@@ -263,49 +290,55 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
     }
   };
 
-  // Pipeline over the stages t of this split (buffers and register sets are
-  // indexed by t, all compile-time constants in the unrolled loop).  Step t:
-  // issue the loads of X(t + 3) and W(t + 4); multiply stage t from LDS
-  // buffer t % 2; decode the raw codes of stage t + 1 into buffer (t + 1) % 2;
-  // convert X(t + 1) into buffer (t + 1) % 2; put the raw codes of stage t + 2
-  // into raw buffer t % 2; barrier.  Loads have two steps to arrive.
-  XRegs rx[3];
-  WRegs rw[3];
 #define Q4_STEP(I)                                          \
   do {                                                      \
-    load_x(t + (I) + 3, rx[(I) % 3]);                       \
-    load_w(t + (I) + 4, rw[(I) % 3]);                       \
+    load_x(t + (I) + D, (I) % D);                           \
+    load_w(t + (I) + D + 1, (I) % D);                       \
     __builtin_amdgcn_sched_barrier(0);                      \
     compute((I) % 2);                                       \
     decode(((I) + 1) % 2);                                  \
-    store_x(rx[((I) + 1) % 3], ((I) + 1) % 2);              \
-    store_w(rw[((I) + 1) % 3], (I) % 2);                    \
+    store_x(((I) + 1) % D, ((I) + 1) % 2);                  \
+    store_w(((I) + 1) % D, (I) % 2);                        \
     __syncthreads();                                        \
   } while (0)
 
-  load_x(0, rx[0]);
-  load_w(0, rw[0]);
-  load_w(1, rw[1]);
-  store_w(rw[0], 0);
-  store_w(rw[1], 1);
-  store_x(rx[0], 0);
-  load_x(1, rx[1]);
-  load_w(2, rw[1]);
-  load_x(2, rx[2]);
-  load_w(3, rw[2]);
+  // prologue: stage 0 converted, raw codes of stages 0 and 1 in LDS, stage 0
+  // decoded; X(1 .. D-1) and W(2 .. D) in flight in ring slots 1 .. D-1.
+  load_x(0, 0);
+  load_w(0, 0);
+  load_w(1, 1);
+  store_w(0, 0);
+  store_w(1, 1);
+  store_x(0, 0);
+#pragma unroll
+  for (int i = 1; i < D; ++i) {
+    load_x(i, i);
+    load_w(i + 1, i);
+  }
   __syncthreads();
   decode(0);
   __syncthreads();
   int t = 0;
-  for (; t + 6 <= nst; t += 6) {
-    Q4_STEP(0); Q4_STEP(1); Q4_STEP(2); Q4_STEP(3); Q4_STEP(4); Q4_STEP(5);
+  if constexpr (D == 3) {
+    for (; t + 6 <= nst; t += 6) {
+      Q4_STEP(0); Q4_STEP(1); Q4_STEP(2); Q4_STEP(3); Q4_STEP(4); Q4_STEP(5);
+    }
+    const int rem = nst - t;  // uniform; at most five more steps
+    if (rem > 0) Q4_STEP(0);
+    if (rem > 1) Q4_STEP(1);
+    if (rem > 2) Q4_STEP(2);
+    if (rem > 3) Q4_STEP(3);
+    if (rem > 4) Q4_STEP(4);
+  } else {
+    static_assert(D == 4, "prefetch depth 3 or 4");
+    for (; t + 4 <= nst; t += 4) {
+      Q4_STEP(0); Q4_STEP(1); Q4_STEP(2); Q4_STEP(3);
+    }
+    const int rem = nst - t;  // uniform; at most three more steps
+    if (rem > 0) Q4_STEP(0);
+    if (rem > 1) Q4_STEP(1);
+    if (rem > 2) Q4_STEP(2);
   }
-  const int rem = nst - t;  // uniform; at most five more steps
-  if (rem > 0) Q4_STEP(0);
-  if (rem > 1) Q4_STEP(1);
-  if (rem > 2) Q4_STEP(2);
-  if (rem > 3) Q4_STEP(3);
-  if (rem > 4) Q4_STEP(4);
 #undef Q4_STEP
 
   // 16 x 16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + v.
@@ -453,13 +486,19 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 
 }  // namespace
 
-// K-split plan of the main kernel: enough workgroups for two per CU when the
-// tile count alone does not give them, at least 8 stages (512 of K) per
-// split, at most MAX_SPLITS, and never a partial buffer beyond ws_bytes.
-static int plan_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, int* stages) {
-  const int64_t ntiles = ((M + T_BM - 1) / T_BM) * ((N + T_BN - 1) / T_BN);
+// Tile width of the main kernel for a shape: 256-wide tiles halve the X
+// traffic per flop but give half as many tiles (one workgroup per CU).
+static int pick_bn(int64_t N) { return N >= 512 ? 256 : 128; }
+
+// K-split plan: enough workgroups to fill every workgroup slot of the GPU
+// when the tile count alone does not, at least 8 stages (512 of K) per split,
+// at most MAX_SPLITS, and never a partial buffer beyond ws_bytes.
+static int plan_splits(int64_t M, int64_t N, int64_t K, int bn, int cus, size_t ws_bytes,
+                       int* stages) {
+  const int64_t ntiles = ((M + T_BM - 1) / T_BM) * ((N + bn - 1) / bn);
   const int nbp = static_cast<int>(K / 64);
-  int64_t want = (2 * static_cast<int64_t>(cus)) / ntiles;
+  const int64_t slots = static_cast<int64_t>(cus) * (bn == 128 ? 2 : 1);
+  int64_t want = slots / ntiles;
   want = std::min<int64_t>(want, nbp / 8);
   want = std::min<int64_t>(want, MAX_SPLITS);
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
@@ -476,22 +515,32 @@ static int plan_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
   if (K % 64 != 0) return 0;
   int stages = 0;
-  const int splits = plan_splits(M, N, K, cus, SIZE_MAX, &stages);
+  const int splits = plan_splits(M, N, K, pick_bn(N), cus, SIZE_MAX, &stages);
   return splits > 1 ? static_cast<size_t>(splits) * M * N * sizeof(float) : 0;
+}
+
+template <int BN, int D>
+static void launch_tile(const uint8_t* w, const float* x, float* y, float* P, int64_t M,
+                        int64_t N, int64_t K, int splits, int stages, hipStream_t s) {
+  const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+  const int tiles_m = static_cast<int>((M + T_BM - 1) / T_BM);
+  const int ntiles = tiles_n * tiles_m;
+  hipLaunchKernelGGL((matmul_tile_kernel<BN, D>), dim3(ntiles * splits),
+                     dim3(TileCfg<BN>::THREADS), 0, s, w, x, y, P, static_cast<int>(M),
+                     static_cast<int>(N), static_cast<int>(K), tiles_n, ntiles, stages);
 }
 
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
   if (K % 64 == 0) {
-    const int tiles_n = static_cast<int>((N + T_BN - 1) / T_BN);
-    const int tiles_m = static_cast<int>((M + T_BM - 1) / T_BM);
-    const int ntiles = tiles_n * tiles_m;
+    const int bn = pick_bn(N);
     int stages = 0;
-    const int splits = plan_splits(M, N, K, cus, ws ? ws_bytes : 0, &stages);
+    const int splits = plan_splits(M, N, K, bn, cus, ws ? ws_bytes : 0, &stages);
     float* P = splits > 1 ? static_cast<float*>(ws) : nullptr;
-    hipLaunchKernelGGL(matmul_tile_kernel, dim3(ntiles * splits), dim3(T_THREADS), 0, s, w, x, y,
-                       P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
-                       ntiles, stages);
+    if (bn == 256)
+      launch_tile<256, 4>(w, x, y, P, M, N, K, splits, stages, s);
+    else
+      launch_tile<128, 3>(w, x, y, P, M, N, K, splits, stages, s);
     if (splits > 1) {
       const int64_t mn = M * N;
       const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;

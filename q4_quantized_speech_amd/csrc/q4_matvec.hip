@@ -20,7 +20,8 @@
 //    y += d * (sum_j q_j x_j - 8 * S_b);
 //  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
 //    sums are then added in LDS in a fixed order (deterministic results);
-//  * workgroups are persistent (a grid-stride loop over row groups).
+//  * workgroups are persistent (a grid-stride loop over row groups), as many
+//    as are resident at once, with the passes spread evenly over them.
 // The argmax variant (the LM head over the 131072-row table that section
 // "Solutions techniques", item 3, keeps in Q4) tracks the best (value, lowest
 // index) per lane and reduces it per workgroup into a workspace slot; a small
@@ -302,9 +303,12 @@ int64_t launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, f
       nb = 1;
     per_cu = nb;
   }
-  const int64_t cap = static_cast<int64_t>(device_info().cu_count) * per_cu;
-  int64_t g = passes < cap ? passes : cap;
-  if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
+  // Balanced: the fewest passes per workgroup that fit the resident
+  // workgroups, spread evenly (an uneven last round costs a whole pass).
+  int64_t cap = static_cast<int64_t>(device_info().cu_count) * per_cu;
+  if (ARGMAX && cap > AM_MAX_PARTIALS) cap = AM_MAX_PARTIALS;
+  const int64_t rounds = (passes + cap - 1) / cap;
+  const int64_t g = (passes + rounds - 1) / rounds;
   hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX>), dim3(static_cast<unsigned>(g), M),
                      dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
   return g;

@@ -11,7 +11,8 @@
 //    pair column for the whole kernel;
 //  * that lane keeps its 64 x values and the two block sums S_b (sum of x over
 //    block b) in registers: x is read from memory once per lane, never from LDS;
-//  * each lane serves R = 2 rows per pass (4 DPP rows per wave -> 8 rows);
+//  * each lane serves R = 2 rows per pass (4 DPP rows per wave -> 8 rows), or
+//    R = 1 where the finer passes spread a short matrix over more CUs;
 //    passes are double-buffered with two register sets used alternately, so
 //    the in-order vmcnt counter lets the next pass's loads fly while the
 //    current one computes;
@@ -34,7 +35,6 @@ namespace q4 {
 namespace {
 
 constexpr int AM_MAX_PARTIALS = 2048;  // per-row partials of the argmax reduction
-constexpr int MV_R = 2;                // rows per lane per pass
 
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -105,12 +105,11 @@ __global__ __launch_bounds__(256) void argmax_fold_kernel(const void* workspace,
 }
 
 // Pair kernel: K % 64 == 0, K <= 12288, KS = ceil(K / 1024) waves per workgroup.
-template <int KS, bool ARGMAX>
+template <int KS, bool ARGMAX, int R>
 __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
     int K) {
-  constexpr int R = MV_R;
   constexpr int ROWS = 4 * R;  // rows per pass
   __shared__ float red[2][KS][ROWS];
   const int m = blockIdx.y;
@@ -287,31 +286,52 @@ __global__ __launch_bounds__(256) void matvec_any_kernel(
   if constexpr (ARGMAX) am_write_partial(bv, bi, m, workspace);
 }
 
-// Returns the number of workgroups per row of x (argmax partials).
-template <int KS, bool ARGMAX>
-int64_t launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
-                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const int64_t rows = 4 * MV_R;
-  const int64_t passes = (N + rows - 1) / rows;
-  // A persistent grid must not exceed what is resident at once: a second,
-  // partial round of workgroups costs far more than it adds.
+// Grid of the pair kernel with R rows per lane: the fewest passes per
+// workgroup that fit the resident workgroups, spread evenly (an uneven last
+// round costs a whole pass).  A persistent grid must not exceed what is
+// resident at once: a second, partial round of workgroups costs far more than
+// it adds.
+struct PairGrid {
+  int64_t g;         // workgroups
+  int64_t cu_rows;   // rows handled by the busiest CU
+};
+template <int KS, bool ARGMAX, int R>
+PairGrid pair_grid(int64_t N) {
   static int per_cu = 0;  // per process; the kernel's resource use is fixed
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX>, 64 * KS,
-                                                      0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R>,
+                                                      64 * KS, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
   }
-  // Balanced: the fewest passes per workgroup that fit the resident
-  // workgroups, spread evenly (an uneven last round costs a whole pass).
-  int64_t cap = static_cast<int64_t>(device_info().cu_count) * per_cu;
+  const int64_t cus = device_info().cu_count;
+  const int64_t passes = (N + 4 * R - 1) / (4 * R);
+  int64_t cap = cus * per_cu;
   if (ARGMAX && cap > AM_MAX_PARTIALS) cap = AM_MAX_PARTIALS;
   const int64_t rounds = (passes + cap - 1) / cap;
   const int64_t g = (passes + rounds - 1) / rounds;
-  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX>), dim3(static_cast<unsigned>(g), M),
+  return PairGrid{g, ((g + cus - 1) / cus) * rounds * 4 * R};
+}
+
+// Two rows per lane amortise the per-pass reductions and the per-workgroup
+// start-up (each workgroup loads its x slices); one row per lane halves the
+// pass granularity.  Use one row only where two would leave CUs idle and one
+// gives the busiest CU fewer rows.  Returns the number of workgroups per row
+// of x (argmax partials).
+template <int KS, bool ARGMAX>
+int64_t launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
+                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const PairGrid g2 = pair_grid<KS, ARGMAX, 2>(N);
+  const PairGrid g1 = pair_grid<KS, ARGMAX, 1>(N);
+  if (g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows) {
+    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1>), dim3(static_cast<unsigned>(g1.g), M),
+                       dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
+    return g1.g;
+  }
+  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2>), dim3(static_cast<unsigned>(g2.g), M),
                      dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
-  return g;
+  return g2.g;
 }
 
 template <bool ARGMAX>

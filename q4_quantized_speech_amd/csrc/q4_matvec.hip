@@ -15,9 +15,11 @@
 //    R = 1 where the finer passes spread a short matrix over more CUs;
 //    passes are double-buffered with two register sets used alternately, so
 //    the in-order vmcnt counter lets the next pass's loads fly while the
-//    current one computes;
+//    current one computes; rows are read through a range-checked buffer
+//    resource based at the pass's first row;
 //  * codes become floats with v_cvt_f32_ubyte (one op per weight) and are
-//    accumulated as sum q*x; the -8 offset is applied per block:
+//    accumulated as sum q*x, the high nibbles taken in place as 16 q against
+//    x / 16 (one mask per code dword); the -8 offset is applied per block:
 //    y += d * (sum_j q_j x_j - 8 * S_b);
 //  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
 //    sums are then added in LDS in a fixed order (deterministic results);
@@ -36,15 +38,6 @@ namespace {
 
 constexpr int AM_MAX_PARTIALS = 2048;  // per-row partials of the argmax reduction
 
-typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
-
-__device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t (&w)[9]) {
-  const u32x4a a = *reinterpret_cast<const u32x4a*>(p);
-  const u32x4a b = *reinterpret_cast<const u32x4a*>(p + 16);
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-  w[8] = *reinterpret_cast<const uint32_t*>(p + 32);
-}
 
 // Argmax bookkeeping: idx < 0 means "no candidate"; NaN never wins.
 __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
@@ -122,15 +115,28 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
   const int c = cvalid ? craw : nbp - 1;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS;
 
-  // weights of the first pass, then this lane's x slice (64 floats) and sums
+  // Weights of the first pass, then this lane's x slice (64 floats) and sums.
+  // A pass's rows are read through a range-checked buffer resource based at
+  // its first row (uniform), so each lane keeps constant offsets and rows past
+  // N read as zeros (they are never stored).
   int64_t row0 = static_cast<int64_t>(blockIdx.x) * ROWS;
   uint32_t wa[R][9], wb[R][9];
+  int wvo[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    wvo[r] = static_cast<int>((grp * R + r) * rb) + c * PAIR_BYTES;
   auto load = [&](int64_t r0, uint32_t (&w)[R][9]) {
+    const int64_t left = N - r0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W + (left > 0 ? r0 : 0) * rb), 0,
+        left > 0 ? static_cast<int>((left < ROWS ? left : ROWS) * rb) : 0, 0x00020000);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      int64_t row = r0 + grp * R + r;
-      row = row < N ? row : N - 1;
-      load_pair(W + row * rb + static_cast<int64_t>(c) * PAIR_BYTES, w[r]);
+      const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, wvo[r], 0, 0));
+      const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, wvo[r], 16, 0));
+      w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+      w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
+      w[r][8] = __builtin_amdgcn_raw_buffer_load_b32(rs, wvo[r], 32, 0);
     }
   };
   load(row0, wa);
@@ -152,6 +158,12 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     S1 = b0 + b1;
   }
   if (!cvalid) S0 = S1 = 0.f;
+  // x of the high nibbles, divided by 16 (exact) for nib_dot4_h16
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    xv[16 + t] *= 0.0625f;
+    xv[48 + t] *= 0.0625f;
+  }
 
   // sum over this lane's pair for R rows: d0*(sum q x - 8 S0) + d1*(...)
   auto compute = [&](uint32_t (&w)[R][9], float (&acc)[R]) {
@@ -162,13 +174,13 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
       for (int t = 0; t < 4; ++t) {
         const f32x4 xl = {xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
         const f32x4 xh = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
-        s0 = nib_dot4(shift16(w[r][t + 1], w[r][t]), xl, xh, s0);
+        s0 = nib_dot4_h16(shift16(w[r][t + 1], w[r][t]), xl, xh, s0);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const f32x4 xl = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
         const f32x4 xh = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
-        s1 = nib_dot4(w[r][5 + t], xl, xh, s1);
+        s1 = nib_dot4_h16(w[r][5 + t], xl, xh, s1);
       }
       const float d0 = cvalid ? half_bits_to_float(w[r][0] & 0xFFFFu) : 0.f;
       const float d1 = cvalid ? half_bits_to_float(w[r][4] >> 16) : 0.f;
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     compute(wa, acc);
     finish(row0, acc, 0);
   } else {
-    // ping-pong over passes; loads past the end are clamped to the last row
+    // ping-pong over passes; passes past the end read as zeros (no traffic)
     for (;;) {
       const int64_t r1 = row0 + stride;
       load(r1, wb);

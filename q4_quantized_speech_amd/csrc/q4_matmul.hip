@@ -581,6 +581,170 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel: M <= 16 MT rows of X (MT <= 5), K % 64 == 0.  The decoder's
+// prompt prefix (16 / 38 / 76 tokens) is far below a 128-row tile, and the
+// product is bound by streaming W; so W is the MFMA A operand (16 weight rows
+// per wave, decoded straight into operand registers) and X^T the B operand,
+// shared by the 8 waves of a workgroup (128 weight rows) through LDS.  Per
+// stage of 64 k the workgroup stages the raw codes of its 128 rows and the
+// binary16 X^T of the stage (coalesced loads, a ring of SK_D register sets),
+// then every wave decodes its rows and multiplies against all MT tiles of X.
+// Output lane layout of the 16 x 16 tile: C[n][m] with m = lane % 16 and
+// n = 4 (lane / 16) + v, so each lane writes 4 consecutive columns of Y.
+// ---------------------------------------------------------------------------
+constexpr int SK_ROWS = 128, SK_THREADS = 512, SK_D = 4;
+constexpr int SK_WDW = SK_ROWS * 9;                               // code dwords per stage: 1152
+constexpr int SK_WU = (SK_WDW + SK_THREADS - 1) / SK_THREADS;     // rounds: 3
+constexpr int SK_MAX_MT = 5;
+
+template <int MT>
+__global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
+    const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
+    float* __restrict__ P, int M, int N, int K, int groups, int split_stages) {
+  constexpr int XU = (MT * 256 + SK_THREADS - 1) / SK_THREADS;  // 16-byte X chunks per thread
+  __shared__ f16x8 Xs[2][2][MT][64];  // [buf][block][m tile][element]
+  __shared__ uint32_t Wraw[2][SK_WDW];
+
+  const int item = xcd_tile(blockIdx.x, gridDim.x);
+  const int split = item / groups, grp = item % groups;
+  const int n0 = grp * SK_ROWS;
+  const int nbp = K >> 6;
+  const int s0 = split * split_stages;
+  const int nst = min(nbp - s0, split_stages);  // >= 1 (host guarantees)
+  const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // X staging: chunk c = tid + 512 u (row c / 16, 16-byte chunk c % 16);
+  // rows past M read as zeros.  Same operand order and swizzle as the tile
+  // kernels: slot g of row r (block b) at element 16 g + (r % 16 ^ (g + 4 b)).
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, static_cast<int64_t>(M) * K * 4);
+  int xvo[XU], xlds[XU];
+  bool xon[XU];
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int c = tid + SK_THREADS * u;
+    const int r = c >> 4, j = c & 15;
+    const int xb = j >> 3, xh = (j >> 2) & 1, xg = j & 3;
+    xon[u] = c < MT * 256;  // wave-uniform
+    xvo[u] = r * K * 4 + j * 16;
+    xlds[u] = ((xb * MT + (r >> 4)) * 64 + 16 * xg + ((r & 15) ^ (xg + 4 * xb))) * 16 + 8 * xh;
+  }
+  // W staging: flat code dword f = tid + 512 u of the stage (row f / 9)
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + static_cast<int64_t>(n0) * rb,
+                                               static_cast<int64_t>(N - n0) * rb);
+  int wvo[SK_WU];
+#pragma unroll
+  for (int u = 0; u < SK_WU; ++u) {
+    const int f = tid + SK_THREADS * u;
+    wvo[u] = static_cast<int>((f / 9) * rb) + (f % 9) * 4;
+  }
+  const bool wlast = tid < SK_WDW - (SK_WU - 1) * SK_THREADS;  // wave-uniform
+
+  f32x4 rx[SK_D][XU];
+  uint32_t rw[SK_D][SK_WU];
+  auto load = [&](int t, int slot) {
+    const int st = s0 + (t < nst ? t : nst - 1);
+#pragma unroll
+    for (int u = 0; u < XU; ++u)
+      if (xon[u])
+        rx[slot][u] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[u], st * 256, 0));
+#pragma unroll
+    for (int u = 0; u < SK_WU - 1; ++u)
+      rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u], st * PAIR_BYTES, 0);
+    if (wlast)
+      rw[slot][SK_WU - 1] =
+          __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[SK_WU - 1], st * PAIR_BYTES, 0);
+  };
+  // ordering guard (see the tile kernels): volatile first ops on loaded data
+  auto pk_f16 = [](float a, float b) -> uint32_t {
+    uint32_t r;
+    asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  };
+  auto pin = [](uint32_t v) -> uint32_t {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+  };
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  auto store = [&](int slot, int buf) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u)
+      if (xon[u]) {
+        const f32x4 v = rx[slot][u];
+        const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(&Xs[buf][0][0][0]) + xlds[u]) = h;
+      }
+#pragma unroll
+    for (int u = 0; u < SK_WU - 1; ++u) Wraw[buf][tid + SK_THREADS * u] = pin(rw[slot][u]);
+    if (wlast) Wraw[buf][tid + SK_THREADS * (SK_WU - 1)] = pin(rw[slot][SK_WU - 1]);
+  };
+
+  // this wave's rows: n0 + 16 wave + lane % 16; lane group g = lane / 16
+  const int nl = lane & 15, g = lane >> 4;
+  const int wbase = (16 * wave + nl) * 9;
+  const int xe0 = 16 * g + (nl ^ g), xe1 = 16 * g + (nl ^ (g + 4));
+  f32x4v acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+    const uint32_t* wr = &Wraw[buf][wbase];
+    const uint32_t q0a = wr[g], q0b = wr[g + 1], d01 = wr[0], d1w = wr[4], q1 = wr[5 + g];
+    const f16x8 a0 = decode8_f16(shift16(q0b, q0a), d01 & 0xFFFFu);
+    const f16x8 a1 = decode8_f16(q1, d1w >> 16);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Xs[buf][0][i][xe0], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Xs[buf][1][i][xe1], acc[i], 0, 0, 0);
+    }
+  };
+
+  // Step t: issue the loads of stage t + D; stage t + 1 (loaded D - 1 steps
+  // ago) into LDS buffer (t + 1) % 2; multiply stage t from buffer t % 2;
+  // barrier.
+#define Q4_SSTEP(I)                                         \
+  do {                                                      \
+    load(t + (I) + SK_D, (I) % SK_D);                       \
+    __builtin_amdgcn_sched_barrier(0);                      \
+    store(((I) + 1) % SK_D, ((I) + 1) % 2);                 \
+    compute((I) % 2);                                       \
+    __syncthreads();                                        \
+  } while (0)
+
+#pragma unroll
+  for (int i = 0; i < SK_D; ++i) load(i, i);
+  store(0, 0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 4 <= nst; t += 4) {
+    Q4_SSTEP(0); Q4_SSTEP(1); Q4_SSTEP(2); Q4_SSTEP(3);
+  }
+  const int rem = nst - t;  // uniform; at most three more steps
+  if (rem > 0) Q4_SSTEP(0);
+  if (rem > 1) Q4_SSTEP(1);
+  if (rem > 2) Q4_SSTEP(2);
+#undef Q4_SSTEP
+
+  // Y[m][n] for m = 16 i + lane % 16, n = n0 + 16 wave + 4 (lane / 16) + v
+  float* out = P ? P + static_cast<int64_t>(split) * M * N : Y;
+  const int nb = n0 + 16 * wave + 4 * g;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = 16 * i + nl;
+    if (m >= M) continue;
+    float* yr = out + static_cast<int64_t>(m) * N + nb;
+    if ((N & 3) == 0 && nb + 4 <= N) {
+      *reinterpret_cast<f32x4v*>(yr) = acc[i];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (nb + v < N) yr[v] = acc[i][v];
+    }
+  }
+}
+
 // Y = sum over s of P[s] in the order s = 0, 1, ... (deterministic).
 __global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restrict__ P,
                                                           float* __restrict__ Y, int64_t mn,
@@ -707,37 +871,55 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 
 }  // namespace
 
-// Tile width of the main kernel for a shape: 256-wide tiles halve the X
-// traffic per flop but give half as many tiles (one workgroup per CU).
-static int pick_bn(int64_t N) { return N >= 512 ? 256 : 128; }
+// Kernel and K-split plan for a shape.
+enum MatmulKind { MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
+struct MatmulPlan {
+  MatmulKind kind;
+  int splits;  // >= 1
+  int stages;  // stages of 64 per split
+};
 
-// K-split plan: enough workgroups to fill every workgroup slot of the GPU
-// when the tile count alone does not, at least 8 stages (512 of K) per split,
-// at most MAX_SPLITS, and never a partial buffer beyond ws_bytes.
-static int plan_splits(int64_t M, int64_t N, int64_t K, int bn, int cus, size_t ws_bytes,
-                       int* stages) {
-  const int64_t ntiles = ((M + T_BM - 1) / T_BM) * ((N + bn - 1) / bn);
+// Skinny for prompt-prefix row counts (bound by streaming W); 128 x 256
+// wave-specialised tiles for wide outputs (half the X traffic per flop of
+// 128 x 128); 128 x 128 tiles otherwise.  K is split when the units alone
+// cannot fill every workgroup slot: at least `min_st` stages per split, at
+// most MAX_SPLITS, for the skinny kernel no more partial bytes than weight
+// bytes, and never more than the workspace holds.
+static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+  if (K % 64 != 0) return MatmulPlan{MM_SIMPLE, 1, 0};
   const int nbp = static_cast<int>(K / 64);
-  const int64_t slots = static_cast<int64_t>(cus) * (bn == 128 ? 2 : 1);
-  int64_t want = slots / ntiles;
-  want = std::min<int64_t>(want, nbp / 8);
-  want = std::min<int64_t>(want, MAX_SPLITS);
+  MatmulKind kind;
+  int64_t units, slots, min_st, cap = MAX_SPLITS;
+  if (M <= 16 * SK_MAX_MT) {
+    kind = MM_SKINNY;
+    units = (N + SK_ROWS - 1) / SK_ROWS;
+    slots = 2 * static_cast<int64_t>(cus);
+    min_st = 4;
+    cap = std::max<int64_t>(1, (K * 9 / 16) / (4 * M));
+  } else if (N >= 512) {
+    kind = MM_WIDE;
+    units = ((M + T_BM - 1) / T_BM) * ((N + WS_BN - 1) / WS_BN);
+    slots = cus;
+    min_st = 8;
+  } else {
+    kind = MM_TILE;
+    units = ((M + T_BM - 1) / T_BM) * ((N + 127) / 128);
+    slots = 2 * static_cast<int64_t>(cus);
+    min_st = 8;
+  }
+  int64_t want = slots / units;
+  want = std::min<int64_t>(want, nbp / min_st);
+  want = std::min<int64_t>(want, std::min<int64_t>(cap, MAX_SPLITS));
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
   while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
-  if (want < 2) {
-    *stages = nbp;
-    return 1;
-  }
+  if (want < 2) return MatmulPlan{kind, 1, nbp};
   const int per = static_cast<int>((nbp + want - 1) / want);
-  *stages = per;
-  return (nbp + per - 1) / per;  // every split non-empty
+  return MatmulPlan{kind, (nbp + per - 1) / per, per};  // every split non-empty
 }
 
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
-  if (K % 64 != 0) return 0;
-  int stages = 0;
-  const int splits = plan_splits(M, N, K, pick_bn(N), cus, SIZE_MAX, &stages);
-  return splits > 1 ? static_cast<size_t>(splits) * M * N * sizeof(float) : 0;
+  const MatmulPlan p = plan_matmul(M, N, K, cus, SIZE_MAX);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
 }
 
 template <int BN, int D>
@@ -751,33 +933,55 @@ static void launch_tile(const uint8_t* w, const float* x, float* y, float* P, in
                      static_cast<int>(N), static_cast<int>(K), tiles_n, ntiles, stages);
 }
 
+template <int MT>
+static void launch_skinny(const uint8_t* w, const float* x, float* y, float* P, int64_t M,
+                          int64_t N, int64_t K, int splits, int stages, hipStream_t s) {
+  const int groups = static_cast<int>((N + SK_ROWS - 1) / SK_ROWS);
+  hipLaunchKernelGGL((matmul_skinny_kernel<MT>), dim3(groups * splits), dim3(SK_THREADS), 0, s,
+                     w, x, y, P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                     groups, stages);
+}
+
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
-  if (K % 64 == 0) {
-    const int bn = pick_bn(N);
-    int stages = 0;
-    const int splits = plan_splits(M, N, K, bn, cus, ws ? ws_bytes : 0, &stages);
-    float* P = splits > 1 ? static_cast<float*>(ws) : nullptr;
-    if (bn == 256) {
+  const MatmulPlan p = plan_matmul(M, N, K, cus, ws ? ws_bytes : 0);
+  float* P = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  switch (p.kind) {
+    case MM_SKINNY:
+      switch ((M + 15) / 16) {
+        case 1: launch_skinny<1>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+        case 2: launch_skinny<2>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+        case 3: launch_skinny<3>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+        case 4: launch_skinny<4>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+        default: launch_skinny<5>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+      }
+      break;
+    case MM_WIDE: {
       const int tiles_n = static_cast<int>((N + WS_BN - 1) / WS_BN);
       const int ntiles = tiles_n * static_cast<int>((M + T_BM - 1) / T_BM);
-      hipLaunchKernelGGL(matmul_ws_kernel, dim3(ntiles * splits), dim3(WS_THREADS), 0, s, w, x, y,
-                         P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
-                         ntiles, stages);
-    } else {
-      launch_tile<128, 3>(w, x, y, P, M, N, K, splits, stages, s);
+      hipLaunchKernelGGL(matmul_ws_kernel, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s, w, x,
+                         y, P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                         tiles_n, ntiles, p.stages);
+      break;
     }
-    if (splits > 1) {
-      const int64_t mn = M * N;
-      const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
-      const int blocks = static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
-      hipLaunchKernelGGL(splitk_fold_kernel, dim3(blocks), dim3(256), 0, s, P, y, mn, splits);
+    case MM_TILE:
+      launch_tile<128, 3>(w, x, y, P, M, N, K, p.splits, p.stages, s);
+      break;
+    case MM_SIMPLE: {
+      const dim3 grid(static_cast<unsigned>((N + S_BN - 1) / S_BN),
+                      static_cast<unsigned>((M + S_BM - 1) / S_BM));
+      hipLaunchKernelGGL(matmul_simple_kernel, grid, dim3(S_THREADS), 0, s, w, x, y,
+                         static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+      break;
     }
-  } else {
-    const dim3 grid(static_cast<unsigned>((N + S_BN - 1) / S_BN),
-                    static_cast<unsigned>((M + S_BM - 1) / S_BM));
-    hipLaunchKernelGGL(matmul_simple_kernel, grid, dim3(S_THREADS), 0, s, w, x, y,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  }
+  if (p.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t mn = M * N;
+    const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
+    const int blocks = static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
+    hipLaunchKernelGGL(splitk_fold_kernel, dim3(blocks), dim3(256), 0, s, P, y, mn, p.splits);
   }
   return hipGetLastError();
 }

@@ -238,6 +238,22 @@ def test_matmul_split_k(m, n, k):
         assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), tag
 
 
+@pytest.mark.parametrize("m", [1, 16, 17, 48, 80, 81])
+@pytest.mark.parametrize("n,k", [(100, 128), (257, 2048), (130, 640)])
+def test_matmul_skinny_edges(m, n, k):
+    """Row counts at the skinny kernel's tile edges (16 per MFMA tile, up to
+    80) and just past it (81 goes to the 128-row tiles); ragged N; with the
+    planned workspace (K split where planned) and without one."""
+    qb = O.quantize_q4_0(_rand_w(n, k, 7 * m + n + k))
+    x = _rand_x(m, k, 5 + m)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    for ws in (True, None):
+        announce(f"matmul skinny edge {m}x{n}x{k} workspace={ws is not None}")
+        y = host(q4.matmul(wq, xd, workspace=ws))
+        assert_within(y, ref, b, *MF, f"skinny {m}x{n}x{k} ws={ws is not None}")
+
+
 def test_matmul_split_k_stays_in_bounds():
     """Partial sums stay inside the workspace, results inside Y."""
     m, n, k = 70, 150, 2048

@@ -106,8 +106,10 @@ class GraphTimer:
                 fn(i)
         torch.cuda.synchronize()
 
-    def time_us(self, reps, warmup=3):
-        """Mean microseconds per captured call over `reps` replays."""
+    def time_us(self, reps, warmup=10):
+        """Mean microseconds per captured call over `reps` replays, after
+        `warmup` untimed replays (the first replays over freshly written weight
+        copies run several percent slow)."""
         ev = self.torch.cuda.Event
         with self.torch.cuda.stream(self.stream):
             for _ in range(warmup):

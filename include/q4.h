@@ -132,11 +132,15 @@ q4_status q4_embed_rows(const void* table_q4, const int32_t* ids, float* out,
  *   w_q4    : N rows of Q4_0.   x : [M, K] float32.
  *   out_idx : M int32 (device).  out_val : M float32 (device) or NULL.
  *   workspace, ws_bytes : device scratch of at least
- *             q4_lmhead_argmax_workspace_bytes(M, N, K) bytes (per-workgroup
- *             partial maxima; any initial contents).  Calls that share a
- *             workspace must be ordered (same stream or synchronised).
- * Two launches on the stream: the streaming pass, then a fold of the
- * per-workgroup partials in a fixed order (deterministic).
+ *             q4_lmhead_argmax_workspace_bytes(M, N, K) bytes (256 per row
+ *             of x).  It must be zero before the first call; every call that
+ *             completes leaves it zero again, so it can be reused without
+ *             clearing.  Calls that share a workspace must be ordered (same
+ *             stream or synchronised).
+ * One launch: each workgroup folds its best (value, lowest index) into a
+ * per-row key with a device-scope atomic max (order-independent, hence
+ * deterministic); the last workgroup to finish writes the outputs and clears
+ * the workspace.
  *   1 <= M <= 64, 1 <= N < 2^31, K a positive multiple of 32.
  * Logits that are NaN are never selected.
  */

@@ -188,11 +188,12 @@ def embed_rows(table_q4: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | No
 
 
 def lmhead_workspace(m: int, device) -> torch.Tensor:
-    """A workspace for lmhead_argmax (any contents; reusable across calls)."""
+    """A zeroed workspace for lmhead_argmax; each call leaves it zeroed, so it
+    can be reused by calls ordered on one stream."""
     nbytes = int(lib().q4_lmhead_argmax_workspace_bytes(m, 0, 0))
     if nbytes == 0:
         raise ValueError("M out of range for lmhead_argmax")
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def lmhead_argmax(w_q4: torch.Tensor, x: torch.Tensor, workspace: torch.Tensor | None = None,

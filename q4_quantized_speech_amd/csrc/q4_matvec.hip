@@ -27,8 +27,9 @@
 //    as are resident at once, with the passes spread evenly over them.
 // The argmax variant (the LM head over the 131072-row table that section
 // "Solutions techniques", item 3, keeps in Q4) tracks the best (value, lowest
-// index) per lane and reduces it per workgroup into a workspace slot; a small
-// second kernel folds the slots in a fixed order.
+// index) per lane, reduces it per workgroup, and folds it into a per-row key
+// in the workspace with one device-scope atomic max; the last workgroup to
+// arrive writes the result and clears the workspace (no second launch).
 
 #include "q4_device.h"
 #include "q4_kernels.h"
@@ -36,7 +37,6 @@
 namespace q4 {
 namespace {
 
-constexpr int AM_MAX_PARTIALS = 2048;  // per-row partials of the argmax reduction
 
 
 // Argmax bookkeeping: idx < 0 means "no candidate"; NaN never wins.
@@ -64,36 +64,47 @@ __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
   }
 }
 
-// Workspace layout: partials [M][AM_MAX_PARTIALS] of uint64
-// {low: float bits of the value, high: index}.  Each workgroup writes its own
-// slot; a second kernel folds them (kernel boundaries order the writes, so no
-// fences or counters are needed and the workspace needs no initial value).
-__device__ __forceinline__ void am_write_partial(float bv, int bi, int m, void* workspace) {
-  uint64_t* partials = reinterpret_cast<uint64_t*>(workspace) + static_cast<int64_t>(m) * AM_MAX_PARTIALS;
-  am_block_reduce(bv, bi);
-  if (threadIdx.x == 0)
-    partials[blockIdx.x] = static_cast<uint64_t>(__float_as_uint(bv)) |
-                           (static_cast<uint64_t>(static_cast<uint32_t>(bi)) << 32);
+// Workspace layout, per row of x (256 bytes, key and counter on separate
+// cache lines): a 64-bit key and a 32-bit arrival counter, both zero between
+// calls.  key = order-preserving bits of the value (high word) | ~index (low
+// word), so the largest key is the largest value with the lowest index, and
+// 0 means "no candidate" (NaN never enters).  Each workgroup folds its
+// candidate in with one device-scope atomic max, waits for it to complete,
+// then counts itself in; the workgroup that arrives last reads the key,
+// writes the outputs and clears both words for the next call.
+constexpr int AM_ROW_BYTES = 256;
+__device__ __forceinline__ uint64_t am_key(float v, int i) {
+  if (i < 0 || v != v) return 0;
+  if (v == 0.f) v = 0.f;  // -0 and +0 tie, like the comparisons above
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
 }
-
-// One workgroup per row of x: fold the partials in a fixed order.
-__global__ __launch_bounds__(256) void argmax_fold_kernel(const void* workspace, int nparts,
-                                                          int32_t* __restrict__ out_idx,
-                                                          float* __restrict__ out_val) {
-  const int m = blockIdx.x;
-  const uint64_t* partials = reinterpret_cast<const uint64_t*>(workspace) + static_cast<int64_t>(m) * AM_MAX_PARTIALS;
-  float v = 0.f;
-  int i = -1;
-  for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
-    const uint64_t e = partials[p];
-    const float ev = __uint_as_float(static_cast<uint32_t>(e));
-    const int ei = static_cast<int>(static_cast<uint32_t>(e >> 32));
-    if (am_better(ev, ei, v, i)) { v = ev; i = ei; }
-  }
-  am_block_reduce(v, i);
+__device__ __forceinline__ void am_publish(float bv, int bi, int m, void* workspace, int nwg,
+                                           int32_t* out_idx, float* out_val) {
+  char* row = reinterpret_cast<char*>(workspace) + static_cast<int64_t>(m) * AM_ROW_BYTES;
+  uint64_t* key = reinterpret_cast<uint64_t*>(row);
+  uint32_t* count = reinterpret_cast<uint32_t*>(row + 128);
+  am_block_reduce(bv, bi);
   if (threadIdx.x == 0) {
-    out_idx[m] = i;
-    if (out_val) out_val[m] = i >= 0 ? v : __builtin_nanf("");
+    __hip_atomic_fetch_max(key, am_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the max is performed before the count moves
+    const uint32_t prev =
+        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == static_cast<uint32_t>(nwg - 1)) {
+      const uint64_t k = __hip_atomic_load(key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(key, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int idx = -1;
+      float val = __builtin_nanf("");
+      if (k != 0) {
+        const uint32_t o = static_cast<uint32_t>(k >> 32);
+        val = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+        idx = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+      }
+      out_idx[m] = idx;
+      if (out_val) out_val[m] = val;
+    }
   }
 }
 
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
       row0 = r2;
     }
   }
-  if constexpr (ARGMAX) am_write_partial(bv, bi, m, workspace);
+  if constexpr (ARGMAX) am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val);
 }
 
 // Generic kernel: any K % 32 == 0 (odd block counts, very long rows).  16
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(256) void matvec_any_kernel(
       if (ok && j == 0) Y[static_cast<int64_t>(m) * N + row] = v;
     }
   }
-  if constexpr (ARGMAX) am_write_partial(bv, bi, m, workspace);
+  if constexpr (ARGMAX) am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val);
 }
 
 // Grid of the pair kernel with R rows per lane: the fewest passes per
@@ -319,8 +330,7 @@ PairGrid pair_grid(int64_t N) {
   }
   const int64_t cus = device_info().cu_count;
   const int64_t passes = (N + 4 * R - 1) / (4 * R);
-  int64_t cap = cus * per_cu;
-  if (ARGMAX && cap > AM_MAX_PARTIALS) cap = AM_MAX_PARTIALS;
+  const int64_t cap = cus * per_cu;
   const int64_t rounds = (passes + cap - 1) / cap;
   const int64_t g = (passes + rounds - 1) / rounds;
   return PairGrid{g, ((g + cus - 1) / cus) * rounds * 4 * R};
@@ -329,21 +339,19 @@ PairGrid pair_grid(int64_t N) {
 // Two rows per lane amortise the per-pass reductions and the per-workgroup
 // start-up (each workgroup loads its x slices); one row per lane halves the
 // pass granularity.  Use one row only where two would leave CUs idle and one
-// gives the busiest CU fewer rows.  Returns the number of workgroups per row
-// of x (argmax partials).
+// gives the busiest CU fewer rows.
 template <int KS, bool ARGMAX>
-int64_t launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
+void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
                      int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const PairGrid g2 = pair_grid<KS, ARGMAX, 2>(N);
   const PairGrid g1 = pair_grid<KS, ARGMAX, 1>(N);
   if (g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows) {
     hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1>), dim3(static_cast<unsigned>(g1.g), M),
                        dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
-    return g1.g;
+    return;
   }
   hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2>), dim3(static_cast<unsigned>(g2.g), M),
                      dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
-  return g2.g;
 }
 
 template <bool ARGMAX>
@@ -351,28 +359,20 @@ hipError_t launch_mv(const uint8_t* w, const float* x, float* y, int32_t* idx, f
                      void* ws, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   // more than 12 waves per workgroup would cap registers below the lane's x slice
   const int64_t ks = (K % 64 == 0 && K <= 12288) ? (K / 64 + 15) / 16 : 0;
-  int64_t g = 0;
   switch (ks) {
 #define Q4_MV_CASE(n) \
-  case n: g = launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
+  case n: launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
     Q4_MV_CASE(1) Q4_MV_CASE(2) Q4_MV_CASE(3) Q4_MV_CASE(4) Q4_MV_CASE(5) Q4_MV_CASE(6)
     Q4_MV_CASE(7) Q4_MV_CASE(8) Q4_MV_CASE(9) Q4_MV_CASE(10) Q4_MV_CASE(11) Q4_MV_CASE(12)
 #undef Q4_MV_CASE
     default: {
       const int cu = device_info().cu_count;
-      g = (N + 15) / 16;
+      int64_t g = (N + 15) / 16;
       const int64_t cap = static_cast<int64_t>(cu) * 8;
       if (g > cap) g = cap;
-      if (ARGMAX && g > AM_MAX_PARTIALS) g = AM_MAX_PARTIALS;
       hipLaunchKernelGGL((matvec_any_kernel<ARGMAX>), dim3(static_cast<unsigned>(g), M), dim3(256),
                          0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
     }
-  }
-  if (ARGMAX) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(argmax_fold_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, ws,
-                       static_cast<int>(g), idx, val);
   }
   return hipGetLastError();
 }
@@ -385,7 +385,7 @@ hipError_t launch_matvec(const uint8_t* w, const float* x, float* y, int64_t M, 
 }
 
 size_t lmhead_workspace_bytes(int64_t M) {
-  return static_cast<size_t>(M) * AM_MAX_PARTIALS * 8;
+  return static_cast<size_t>(M) * AM_ROW_BYTES;
 }
 
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,

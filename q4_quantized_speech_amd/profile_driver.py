@@ -68,8 +68,6 @@ def source_hash() -> str:
 
 def dispatches_per_call(workload: str) -> int:
     """Distinct library kernels one call of the workload launches."""
-    if workload.startswith("lmhead_argmax"):
-        return 2
     if workload.startswith("matmul_"):
         return 0  # one or two (the K-split fold), decided by the shape
     return 1

@@ -321,17 +321,21 @@ def test_lmhead_ties_and_planted():
 
 
 def test_lmhead_workspace_reuse_and_odd_k():
-    n, k = 700, 96
-    qb = O.quantize_q4_0(_rand_w(n, k, 5))
-    ws = q4.lmhead_workspace(1, "cuda")
-    ws.fill_(0xA5)                                # any initial contents
-    wq = dev(qb)
-    for s in range(4):
-        x = _rand_x(1, k, 300 + s)
-        announce(f"lmhead reuse {s}")
-        idx, _ = q4.lmhead_argmax(wq, dev(x), workspace=ws)
-        y, b = O.lmhead_logits(qb, x[0], n, k)
-        assert O.argmax_accepts(y, b, int(host(idx)[0]))
+    """The workspace starts zeroed and every call leaves it zeroed, so calls
+    ordered on one stream can share it; K % 64 == 32 takes the generic kernel."""
+    for (n, k) in [(700, 96), (5000, 3072)]:
+        qb = O.quantize_q4_0(_rand_w(n, k, 5 + k))
+        ws = q4.lmhead_workspace(2, "cuda")
+        wq = dev(qb)
+        for s in range(4):
+            x = _rand_x(2, k, 300 + s)
+            announce(f"lmhead reuse n={n} k={k} call {s}")
+            idx, _ = q4.lmhead_argmax(wq, dev(x), workspace=ws)
+            idx = host(idx)
+            for i in range(2):
+                y, b = O.lmhead_logits(qb, x[i], n, k)
+                assert O.argmax_accepts(y, b, int(idx[i]))
+            assert not host(ws).any(), "workspace not left zeroed"
 
 
 def test_lmhead_full_table():

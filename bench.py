@@ -11,7 +11,9 @@ them).
 The same run also measures, each in its own timed loop: the second half of the
 metric (q4_matmul TFLOP/s over the encoder layer at M = 1500 plus the adapter at
 M = 375), the LM-head argmax and embedding gather over the 131072 x 3072 table,
-the single 3072 x 3072 matvec, and the prefix GEMMs (M = 16 / 38 / 76).  Kernel
+one greedy decode step as a chain (the four projections, the LM-head argmax
+and the embedding row of the chosen token), small batches (M = 2 .. 15), the
+single 3072 x 3072 matvec, and the prefix GEMMs (M = 16 / 38 / 76).  Kernel
 durations come from HIP events recorded on the launch stream around each
 launch.  The CPU baseline is the oracle (float64 dequantise + BLAS dgemv) on a
 bounded sample of the same workload, timed on the host cores.
@@ -203,9 +205,6 @@ def main():
                 "kernel": f"q4_matvec {dominant} {dn}x{dk}",
                 "bytes_per_launch": dom_bytes,
                 "launch_us_mean": per_proj[dominant]["us"]}
-    del copies
-    torch.cuda.empty_cache()
-
     rows = {"decode_layer_projections": per_proj}
 
     def timed(fn, n):
@@ -244,7 +243,48 @@ def main():
     emb = torch.empty((synth.PREFIX_TOKENS, D), device="cuda")
     us = timed(lambda i: q4.embed_rows(tables[i % rt], ids, out=emb, stream=stream), rt)
     rows["embed_rows_38x3072"] = {"us": round(us, 3)}
+
+    # ---------------- one greedy decode step as a chain ----------------
+    # the four projections, the LM-head argmax and the embedding row of the
+    # chosen token (its id read from device memory), back to back on one
+    # stream; weights rotated over the layer and table copies
+    emb1 = torch.empty((1, D), device="cuda")
+
+    def chain_step(i):
+        layer_step(i)
+        q4.lmhead_argmax(tables[i % rt], xl, workspace=ws, out_idx=oi, out_val=ov, stream=stream)
+        q4.embed_rows(tables[i % rt], oi, out=emb1, stream=stream)
+
+    us = timed(chain_step, max(r_layer, rt))
+    chain_bytes = layer_bytes + weight_bytes(V, D) + weight_bytes(1, D)
+    rows["decode_chain_layer_lmhead_embed"] = {
+        "us": round(us, 3), "gbs": round(chain_bytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(chain_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes": chain_bytes}
     del tables, table
+
+    # ---------------- small batches: M = 2 .. 15 over the decoder layer ----------------
+    # q4_matvec re-reads each weight row per row of x (M <= 8); q4_matmul's
+    # skinny kernel reads it once
+    for m in (2, 4, 8, 15):
+        xs = [torch.from_numpy(synth.activations(m, k, synth.seed_for(5, 10 + t))).cuda()
+              for t, (_, n, k) in enumerate(synth.DECODER_LAYER)]
+        ys = [torch.empty((m, n), device="cuda") for (_, n, _) in synth.DECODER_LAYER]
+        wss = [q4.matmul_workspace(m, n, k, "cuda") for (_, n, k) in synth.DECODER_LAYER]
+        row = {}
+        paths = [("matmul", lambda w, x, y, j: q4.matmul(w, x, out=y, workspace=wss[j], stream=stream))]
+        if m <= 8:
+            paths.insert(0, ("matvec", lambda w, x, y, j: q4.matvec(w, x, out=y, stream=stream)))
+        for pname, call in paths:
+            tot = 0.0
+            for j in range(len(synth.DECODER_LAYER)):
+                tot += timed(lambda i, j=j: call(copies[i % r_layer][j], xs[j], ys[j], j), r_layer)
+            row[f"{pname}_layer_us"] = round(tot, 3)
+            row[f"{pname}_layer_weight_gbs"] = round(layer_bytes / (tot * 1e-6) / 1e9, 1)
+        rows[f"small_batch_M{m}"] = row
+        del xs, ys, wss
+    del copies
+    torch.cuda.empty_cache()
     torch.cuda.empty_cache()
 
     # ---------------- matmul: encoder layer at M = 1500 + adapter at 375 ----------------

@@ -297,6 +297,26 @@ def test_matmul_encoder_full(m):
         assert_within(y, ref, b, *MF, f"encoder M={mm} {name}")
 
 
+def test_adapter_on_strided_view_of_encoder_output():
+    """The 4x downsample adapter reads the encoder output in place: rows of 4
+    consecutive frames of width 1280 are one row of 5120 in the same memory
+    (a view, no copy), and the product matches the oracle on those rows."""
+    m = 384
+    _, n_up, k_up = synth.ENCODER_LAYER[1]            # any 1280-wide producer: O 1280x1280
+    q_o = weights_q4(n_up, k_up, synth.seed_for(4, 1))
+    x = synth.activations(m, k_up, synth.seed_for(6, 0))
+    announce("adapter on the encoder output viewed as [M/4, 5120]")
+    enc = q4.matmul(dev(q_o), dev(x))                  # [384, 1280] on the device
+    frames = enc.view(m // 4, 4 * n_up)
+    assert frames.data_ptr() == enc.data_ptr()
+    name, n, k = synth.ADAPTER
+    qa = weights_q4(n, k, synth.seed_for(4, 4))
+    y = host(q4.matmul(dev(qa), frames))
+    xa = host(enc).reshape(m // 4, 4 * n_up)
+    ref, b = O.matmul_f64(qa, xa, n, k)
+    assert_within(y, ref, b, *MF, "adapter on the strided view")
+
+
 # --------------------------------------------------------------------------
 # q4_lmhead_argmax
 # --------------------------------------------------------------------------

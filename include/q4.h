@@ -55,7 +55,10 @@ enum {
     Q4_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 32 != 0            */
     Q4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned           */
     Q4_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
-    Q4_ERR_HIP = 5        /* a HIP call failed; see q4_last_hip_error()        */
+    Q4_ERR_HIP = 5,       /* a HIP call failed; see q4_last_hip_error()        */
+    Q4_ERR_FORMAT = 6,    /* a GGUF file is malformed or uses an unknown form  */
+    Q4_ERR_IO = 7,        /* a file could not be opened or read                */
+    Q4_ERR_NOT_FOUND = 8  /* no such tensor / metadata key / index             */
 };
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -163,6 +166,55 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x,
  */
 q4_status q4_quantize(const float* w, void* w_q4, int64_t N, int64_t K,
                       int32_t* flag, void* stream);
+
+/*
+ * GGUF reader (host code, no GPU) -- the container of the pages' quantised
+ * model (section "Architecture": a GGUF Q4_0 file; section "Préparation du
+ * modèle et sharding": the file is cut into byte pieces of at most 512 MB).
+ *
+ * q4_gguf_open: paths[0 .. npaths-1] are read as ONE byte stream, in order
+ * (one file, or the pieces of a byte-level split).  Parses the header
+ * ("GGUF", version 2 or 3), the metadata, the tensor table and the alignment
+ * ("general.alignment", default 32), and checks that every tensor of a known
+ * element type lies inside the data section.  On success *out owns open file
+ * descriptors until q4_gguf_close.  Errors: Q4_ERR_NULL, Q4_ERR_IO (open or
+ * read failed), Q4_ERR_FORMAT (bad magic or version, truncated or
+ * inconsistent tables, duplicate tensor names, misaligned offsets).
+ *
+ * Tensors: dims[0] is the innermost dimension (a weight of N rows of K is
+ * dims = {K, N, 1, 1}).  Element types sized here: 0 F32, 1 F16, 2 Q4_0,
+ * 8 Q8_0, 30 BF16; other types are listed with nbytes = 0 and cannot be read.
+ * A Q4_0 tensor's bytes are exactly the layout q4_matvec / q4_matmul take.
+ * q4_gguf_read_tensor copies a tensor into HOST memory dst (dst_bytes >=
+ * nbytes, else Q4_ERR_WORKSPACE).  Metadata getters look a key up by name:
+ * integers (any integer or bool type, as int64), floats (F32/F64 as double),
+ * strings (pointer valid until close), arrays (element type and count only).
+ * Returned name/key/string pointers are owned by the handle.  A handle may be
+ * read from several threads at once (pread); open/close are not concurrent
+ * with its use.
+ */
+typedef struct q4_gguf q4_gguf;
+q4_status q4_gguf_open(const char* const* paths, int64_t npaths, q4_gguf** out);
+void q4_gguf_close(q4_gguf* g);
+uint32_t q4_gguf_version(const q4_gguf* g);
+uint64_t q4_gguf_alignment(const q4_gguf* g);
+uint64_t q4_gguf_data_offset(const q4_gguf* g);
+int64_t q4_gguf_tensor_count(const q4_gguf* g);
+int64_t q4_gguf_metadata_count(const q4_gguf* g);
+q4_status q4_gguf_tensor_info(const q4_gguf* g, int64_t index, const char** name,
+                              uint32_t* type, uint32_t* n_dims, int64_t* dims4,
+                              uint64_t* offset, uint64_t* nbytes);
+int64_t q4_gguf_find_tensor(const q4_gguf* g, const char* name);  /* -1: absent */
+q4_status q4_gguf_read_tensor(const q4_gguf* g, int64_t index, void* dst,
+                              uint64_t dst_bytes);
+q4_status q4_gguf_metadata_key(const q4_gguf* g, int64_t index, const char** key,
+                               uint32_t* value_type);
+q4_status q4_gguf_metadata_int(const q4_gguf* g, const char* key, int64_t* value);
+q4_status q4_gguf_metadata_float(const q4_gguf* g, const char* key, double* value);
+q4_status q4_gguf_metadata_string(const q4_gguf* g, const char* key,
+                                  const char** value, uint64_t* length);
+q4_status q4_gguf_metadata_array(const q4_gguf* g, const char* key,
+                                 uint32_t* elem_type, uint64_t* count);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "q4.h")
 QK = 32
 BLOCK_BYTES = 18
 
-Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_HIP = range(6)
+(Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_HIP, Q4_ERR_FORMAT,
+ Q4_ERR_IO, Q4_ERR_NOT_FOUND) = range(9)
 
 
 class Q4Error(RuntimeError):
@@ -60,6 +61,21 @@ _SIGS = {
     "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_quantize": ([_P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "q4_gguf_open": ([_P, _I64, _P], ctypes.c_int),
+    "q4_gguf_close": ([_P], None),
+    "q4_gguf_version": ([_P], ctypes.c_uint32),
+    "q4_gguf_alignment": ([_P], ctypes.c_uint64),
+    "q4_gguf_data_offset": ([_P], ctypes.c_uint64),
+    "q4_gguf_tensor_count": ([_P], _I64),
+    "q4_gguf_metadata_count": ([_P], _I64),
+    "q4_gguf_tensor_info": ([_P, _I64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "q4_gguf_find_tensor": ([_P, ctypes.c_char_p], _I64),
+    "q4_gguf_read_tensor": ([_P, _I64, _P, ctypes.c_uint64], ctypes.c_int),
+    "q4_gguf_metadata_key": ([_P, _I64, _P, _P], ctypes.c_int),
+    "q4_gguf_metadata_int": ([_P, ctypes.c_char_p, _P], ctypes.c_int),
+    "q4_gguf_metadata_float": ([_P, ctypes.c_char_p, _P], ctypes.c_int),
+    "q4_gguf_metadata_string": ([_P, ctypes.c_char_p, _P, _P], ctypes.c_int),
+    "q4_gguf_metadata_array": ([_P, ctypes.c_char_p, _P, _P], ctypes.c_int),
 }
 
 
@@ -231,6 +247,96 @@ def quantize(w: torch.Tensor, out: torch.Tensor | None = None, check: bool = Tru
     if check and int(flag[0].item()) != 0:
         raise ValueError("q4_quantize: non-finite input or a scale overflowing binary16")
     return out
+
+
+GGUF_F32, GGUF_F16, GGUF_Q4_0, GGUF_Q8_0, GGUF_BF16 = 0, 1, 2, 8, 30
+
+
+class Gguf:
+    """A GGUF file (or the ordered byte pieces of one) opened with the
+    library's reader.  ``tensors`` maps name -> (type, dims, offset, nbytes)
+    with dims innermost first; ``read(name)`` returns the tensor's bytes as a
+    numpy uint8 array (a Q4_0 weight of N rows of K as [N, 18*K/32])."""
+
+    def __init__(self, paths):
+        if isinstance(paths, (str, os.PathLike)):
+            paths = [paths]
+        enc = [os.fsencode(p) for p in paths]
+        arr = (ctypes.c_char_p * len(enc))(*enc)
+        h = ctypes.c_void_p()
+        _check(lib().q4_gguf_open(ctypes.cast(arr, ctypes.c_void_p), len(enc), ctypes.byref(h)),
+               "q4_gguf_open")
+        self._h = h
+        self.version = int(lib().q4_gguf_version(h))
+        self.alignment = int(lib().q4_gguf_alignment(h))
+        self.data_offset = int(lib().q4_gguf_data_offset(h))
+        self.tensors = {}
+        for i in range(int(lib().q4_gguf_tensor_count(h))):
+            name, typ, nd = ctypes.c_char_p(), ctypes.c_uint32(), ctypes.c_uint32()
+            dims, off, nb = (ctypes.c_int64 * 4)(), ctypes.c_uint64(), ctypes.c_uint64()
+            _check(lib().q4_gguf_tensor_info(h, i, ctypes.byref(name), ctypes.byref(typ),
+                                             ctypes.byref(nd), dims, ctypes.byref(off),
+                                             ctypes.byref(nb)), "q4_gguf_tensor_info")
+            self.tensors[name.value.decode()] = (int(typ.value), tuple(dims[: nd.value]),
+                                                 int(off.value), int(nb.value))
+        self.metadata = []
+        for i in range(int(lib().q4_gguf_metadata_count(h))):
+            key, vt = ctypes.c_char_p(), ctypes.c_uint32()
+            _check(lib().q4_gguf_metadata_key(h, i, ctypes.byref(key), ctypes.byref(vt)),
+                   "q4_gguf_metadata_key")
+            self.metadata.append((key.value.decode(), int(vt.value)))
+
+    def close(self):
+        if self._h:
+            lib().q4_gguf_close(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+    def read(self, name: str):
+        import numpy as np
+        i = int(lib().q4_gguf_find_tensor(self._h, name.encode()))
+        if i < 0:
+            raise KeyError(name)
+        typ, dims, _, nbytes = self.tensors[name]
+        out = np.empty(nbytes, dtype=np.uint8)
+        _check(lib().q4_gguf_read_tensor(self._h, i, out.ctypes.data_as(ctypes.c_void_p), nbytes),
+               "q4_gguf_read_tensor")
+        if typ == GGUF_Q4_0 and len(dims) == 2:
+            return out.reshape(dims[1], dims[0] // QK * BLOCK_BYTES)
+        return out
+
+    def meta_int(self, key: str) -> int:
+        v = ctypes.c_int64()
+        _check(lib().q4_gguf_metadata_int(self._h, key.encode(), ctypes.byref(v)), "q4_gguf_metadata_int")
+        return int(v.value)
+
+    def meta_float(self, key: str) -> float:
+        v = ctypes.c_double()
+        _check(lib().q4_gguf_metadata_float(self._h, key.encode(), ctypes.byref(v)), "q4_gguf_metadata_float")
+        return float(v.value)
+
+    def meta_string(self, key: str) -> str:
+        v, n = ctypes.c_char_p(), ctypes.c_uint64()
+        _check(lib().q4_gguf_metadata_string(self._h, key.encode(), ctypes.byref(v), ctypes.byref(n)),
+               "q4_gguf_metadata_string")
+        return ctypes.string_at(v, n.value).decode()
+
+    def meta_array(self, key: str):
+        t, n = ctypes.c_uint32(), ctypes.c_uint64()
+        _check(lib().q4_gguf_metadata_array(self._h, key.encode(), ctypes.byref(t), ctypes.byref(n)),
+               "q4_gguf_metadata_array")
+        return int(t.value), int(n.value)
 
 
 def declared_symbols(header: str = HEADER):

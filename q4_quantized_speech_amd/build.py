@@ -1,4 +1,4 @@
-"""Compile the HIP sources into the in-tree shared library libq4mi.so (gfx950).
+"""Compile the HIP (gfx950) and host C++ sources into the in-tree shared library libq4mi.so.
 
 Run as ``python -m q4_quantized_speech_amd.build`` or through
 ``__graft_entry__.build()``.  Every call recompiles.
@@ -38,13 +38,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libq4mi.so)")
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """HIP sources (device and host code) and plain C++ host sources."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [shutil.which("g++") or "g++", *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

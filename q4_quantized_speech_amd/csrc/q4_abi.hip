@@ -49,7 +49,7 @@ using namespace q4;
 
 extern "C" {
 
-int q4_abi_version(void) { return 2; }
+int q4_abi_version(void) { return 3; }
 
 const char* q4_status_string(q4_status status) {
   switch (status) {
@@ -59,6 +59,9 @@ const char* q4_status_string(q4_status status) {
     case Q4_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case Q4_ERR_WORKSPACE: return "workspace missing or too small";
     case Q4_ERR_HIP: return "a HIP call failed (see q4_last_hip_error)";
+    case Q4_ERR_FORMAT: return "malformed or unsupported GGUF content";
+    case Q4_ERR_IO: return "a file could not be opened or read";
+    case Q4_ERR_NOT_FOUND: return "no such tensor, metadata key or index";
     default: return "unknown status";
   }
 }

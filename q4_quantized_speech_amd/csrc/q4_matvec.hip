@@ -10,7 +10,14 @@
 //    KS = ceil(K / 1024) waves of the workgroup, so every lane owns exactly one
 //    pair column for the whole kernel;
 //  * that lane keeps its 64 x values and the two block sums S_b (sum of x over
-//    block b) in registers: x is read from memory once per lane, never from LDS;
+//    block b) in registers.  Each wave reads its 1024-float slice of x once,
+//    coalesced (16 B per lane per load), and hands every lane its 64 values
+//    through LDS: loading them straight from memory would touch 16 cache
+//    lines per load instruction, which costs more address-unit time at the
+//    start of a workgroup than a pass of weights;
+//  * x is requested before the weights and the first two passes of weights
+//    right after, so waiting for x never waits for weights (the memory
+//    counter is in order) and two passes are in flight from the start;
 //  * each lane serves R = 2 rows per pass (4 DPP rows per wave -> 8 rows), or
 //    R = 1 where the finer passes spread a short matrix over more CUs;
 //    passes are double-buffered with two register sets used alternately, so
@@ -150,15 +157,34 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
       w[r][8] = __builtin_amdgcn_raw_buffer_load_b32(rs, wvo[r], 32, 0);
     }
   };
-  load(row0, wa);
-  float xv[64];
+  // x first (coalesced: the wave's 1024-float slice, 16 B per lane per load),
+  // then the weights of the first two passes, so that waiting for x does not
+  // wait for the weights; x goes to this lane's registers through LDS (rows of
+  // 64 floats padded to 68 so the 16 lanes of a DPP row hit distinct banks).
+  __shared__ float xs[KS][16][68];
+  f32x4 xg[4];
   {
-    const f32x4* xg = reinterpret_cast<const f32x4*>(X + static_cast<int64_t>(m) * K + 64 * c);
+    const float* xw = X + static_cast<int64_t>(m) * K + 1024 * ks;
+    const int lim = K - 1024 * ks;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const f32x4 v = xg[t];
-      xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
+    for (int u = 0; u < 4; ++u) {
+      const int p = (u * 64 + (tid & 63)) * 4;
+      xg[u] = p < lim ? *reinterpret_cast<const f32x4*>(xw + p) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
+  load(row0, wa);
+  load(row0 + stride, wb);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = u * 64 + (tid & 63);
+    *reinterpret_cast<f32x4*>(&xs[ks][p >> 4][(p & 15) * 4]) = xg[u];
+  }
+  __syncthreads();
+  float xv[64];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&xs[ks][j][4 * t]);
+    xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
   }
   float S0 = 0.f, S1 = 0.f;
   {
@@ -237,30 +263,23 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     }
   };
 
-  if (row0 + stride >= N) {
-    // one pass per workgroup
+  // ping-pong over passes, two in flight; passes past the end read as zeros
+  // (no traffic)
+  for (;;) {
     float acc[R];
     compute(wa, acc);
     finish(row0, acc, 0);
-  } else {
-    // ping-pong over passes; passes past the end read as zeros (no traffic)
-    for (;;) {
-      const int64_t r1 = row0 + stride;
-      load(r1, wb);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      float acc[R];
-      compute(wa, acc);
-      finish(row0, acc, 0);
-      if (r1 >= N) break;
-      const int64_t r2 = r1 + stride;
-      load(r2, wa);
-      __builtin_amdgcn_sched_barrier(0);
-      float acc2[R];
-      compute(wb, acc2);
-      finish(r1, acc2, 1);
-      if (r2 >= N) break;
-      row0 = r2;
-    }
+    const int64_t r1 = row0 + stride;
+    if (r1 >= N) break;
+    load(r1 + stride, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    float acc2[R];
+    compute(wb, acc2);
+    finish(r1, acc2, 1);
+    row0 = r1 + stride;
+    if (row0 >= N) break;
+    load(row0 + stride, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (ARGMAX) am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val);
 }

@@ -61,26 +61,6 @@ __device__ __forceinline__ float nib_dot4(uint32_t q, f32x4 xl, f32x4 xh, float 
   return acc;
 }
 
-// The same sum with the high-nibble x values given pre-divided by 16
-// (xh16 = xh / 16, exact for normal floats): the high nibbles are taken in
-// place as 16 * q by one mask, so 16 q * (xh / 16) is the product q * xh
-// exactly and every FMA rounds the same value as in nib_dot4.
-__device__ __forceinline__ float nib_dot4_h16(uint32_t q, f32x4 xl, f32x4 xh16, float acc) {
-  uint32_t lo = q & 0x0F0F0F0Fu;
-  uint32_t hi = q & 0xF0F0F0F0u;
-  asm("" : "+v"(lo));
-  asm("" : "+v"(hi));
-  acc = __builtin_fmaf(ubyte_f<0>(lo), xl.x, acc);
-  acc = __builtin_fmaf(ubyte_f<1>(lo), xl.y, acc);
-  acc = __builtin_fmaf(ubyte_f<2>(lo), xl.z, acc);
-  acc = __builtin_fmaf(ubyte_f<3>(lo), xl.w, acc);
-  acc = __builtin_fmaf(ubyte_f<0>(hi), xh16.x, acc);
-  acc = __builtin_fmaf(ubyte_f<1>(hi), xh16.y, acc);
-  acc = __builtin_fmaf(ubyte_f<2>(hi), xh16.z, acc);
-  acc = __builtin_fmaf(ubyte_f<3>(hi), xh16.w, acc);
-  return acc;
-}
-
 // Load block `f` (flat block index over the whole byte array) with 16-bit
 // loads only: works for any block alignment.  d16 = scale bits, qs[4] = the
 // 16 code bytes as little-endian dwords.

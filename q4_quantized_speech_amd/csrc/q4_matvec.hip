@@ -24,10 +24,12 @@
 //    the in-order vmcnt counter lets the next pass's loads fly while the
 //    current one computes; rows are read through a range-checked buffer
 //    resource based at the pass's first row;
-//  * codes become floats with v_cvt_f32_ubyte (one op per weight) and are
-//    accumulated as sum q*x, the high nibbles taken in place as 16 q against
-//    x / 16 (one mask per code dword); the -8 offset is applied per block:
-//    y += d * (sum_j q_j x_j - 8 * S_b);
+//  * codes are masked into half-words as f16 bit patterns (exact subnormals
+//    q * 2^-24, the high nibbles in place as 16 q against x / 16) and fed to
+//    v_fma_mix, which converts and multiply-adds in one instruction per
+//    weight; the two blocks' chains are interleaved so no FMA waits on the
+//    one before it.  The -8 offset is applied per block:
+//    y += d * (2^24 * sum_j q_j 2^-24 x_j - 8 * S_b);
 //  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
 //    sums are then added in LDS in a fixed order (deterministic results);
 //  * workgroups are persistent (a grid-stride loop over row groups), as many
@@ -45,6 +47,45 @@ namespace q4 {
 namespace {
 
 
+
+// Eight codes of one qs dword against x (low nibbles) and x/16 (high
+// nibbles), for two dwords at once.  Each code is masked into a half-word as
+// the f16 bit pattern q (or 16 q): an exact subnormal, q * 2^-24, which
+// v_fma_mix converts for free, so one instruction per weight instead of a
+// byte convert plus an FMA; the sums come out scaled by 2^-24 (exact).  The
+// two chains are interleaved instruction by instruction: a v_fma_mix right
+// after the one it depends on costs a wait state.
+__device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, f32x4 xl0, f32x4 xh0, float& acc0,
+                                              uint32_t q1, f32x4 xl1, f32x4 xh1, float& acc1) {
+  const uint32_t v0 = q0 >> 8, v1 = q1 >> 8;
+  const f16x2 a0 = __builtin_bit_cast(f16x2, q0 & 0x000F000Fu);
+  const f16x2 a1 = __builtin_bit_cast(f16x2, q1 & 0x000F000Fu);
+  const f16x2 b0 = __builtin_bit_cast(f16x2, q0 & 0x00F000F0u);
+  const f16x2 b1 = __builtin_bit_cast(f16x2, q1 & 0x00F000F0u);
+  const f16x2 c0 = __builtin_bit_cast(f16x2, v0 & 0x000F000Fu);
+  const f16x2 c1 = __builtin_bit_cast(f16x2, v1 & 0x000F000Fu);
+  const f16x2 e0 = __builtin_bit_cast(f16x2, v0 & 0x00F000F0u);
+  const f16x2 e1 = __builtin_bit_cast(f16x2, v1 & 0x00F000F0u);
+  float s0 = acc0, s1 = acc1;
+  s0 = __builtin_fmaf(static_cast<float>(a0.x), xl0.x, s0);
+  s1 = __builtin_fmaf(static_cast<float>(a1.x), xl1.x, s1);
+  s0 = __builtin_fmaf(static_cast<float>(c0.x), xl0.y, s0);
+  s1 = __builtin_fmaf(static_cast<float>(c1.x), xl1.y, s1);
+  s0 = __builtin_fmaf(static_cast<float>(a0.y), xl0.z, s0);
+  s1 = __builtin_fmaf(static_cast<float>(a1.y), xl1.z, s1);
+  s0 = __builtin_fmaf(static_cast<float>(c0.y), xl0.w, s0);
+  s1 = __builtin_fmaf(static_cast<float>(c1.y), xl1.w, s1);
+  s0 = __builtin_fmaf(static_cast<float>(b0.x), xh0.x, s0);
+  s1 = __builtin_fmaf(static_cast<float>(b1.x), xh1.x, s1);
+  s0 = __builtin_fmaf(static_cast<float>(e0.x), xh0.y, s0);
+  s1 = __builtin_fmaf(static_cast<float>(e1.x), xh1.y, s1);
+  s0 = __builtin_fmaf(static_cast<float>(b0.y), xh0.z, s0);
+  s1 = __builtin_fmaf(static_cast<float>(b1.y), xh1.z, s1);
+  s0 = __builtin_fmaf(static_cast<float>(e0.y), xh0.w, s0);
+  s1 = __builtin_fmaf(static_cast<float>(e1.y), xh1.w, s1);
+  acc0 = s0;
+  acc1 = s1;
+}
 
 // Argmax bookkeeping: idx < 0 means "no candidate"; NaN never wins.
 __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
@@ -195,7 +236,7 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     S1 = b0 + b1;
   }
   if (!cvalid) S0 = S1 = 0.f;
-  // x of the high nibbles, divided by 16 (exact) for nib_dot4_h16
+  // x of the high nibbles, divided by 16 (exact)
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     xv[16 + t] *= 0.0625f;
@@ -209,20 +250,16 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4 xl = {xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
-        const f32x4 xh = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
-        s0 = nib_dot4_h16(shift16(w[r][t + 1], w[r][t]), xl, xh, s0);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4 xl = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
-        const f32x4 xh = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
-        s1 = nib_dot4_h16(w[r][5 + t], xl, xh, s1);
+        const f32x4 xl0 = {xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
+        const f32x4 xh0 = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
+        const f32x4 xl1 = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
+        const f32x4 xh1 = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
+        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0, w[r][5 + t], xl1, xh1, s1);
       }
       const float d0 = cvalid ? half_bits_to_float(w[r][0] & 0xFFFFu) : 0.f;
       const float d1 = cvalid ? half_bits_to_float(w[r][4] >> 16) : 0.f;
-      acc[r] = __builtin_fmaf(d0, __builtin_fmaf(-8.f, S0, s0), 0.f);
-      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(-8.f, S1, s1), acc[r]);
+      acc[r] = __builtin_fmaf(d0, __builtin_fmaf(s0, 16777216.f, -8.f * S0), 0.f);
+      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(s1, 16777216.f, -8.f * S1), acc[r]);
     }
   };
 

@@ -103,11 +103,14 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  *             planned split on the current device (0: no split planned).  A
  *             smaller workspace gives fewer splits (never an error).  Calls
  *             that share a workspace must be ordered.
- * Weights and activations are rounded to binary16 (round to nearest even) and
- * multiplied on the matrix cores with float32 accumulation, so |x| must stay
- * below 65504.  Deterministic for a given shape, device and ws_bytes; the
- * split changes the order of the float32 sums, so results for different
- * workspace sizes may differ by rounding.
+ * M >= 5: weights and activations are rounded to binary16 (round to nearest
+ * even) and multiplied on the matrix cores with float32 accumulation, so |x|
+ * must stay below 65504.  M <= 4 (several decode streams): the weights enter
+ * the matrix cores exactly (q - 8, block scale applied in float32) and x as
+ * two binary16 parts after a per-chunk power-of-two scaling, which meets the
+ * q4_matvec bound for any finite x.  Deterministic for a given shape, device
+ * and ws_bytes; the split changes the order of the float32 sums, so results
+ * for different workspace sizes may differ by rounding.
  */
 size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 q4_status q4_matmul(const void* w_q4, const float* x, float* y,

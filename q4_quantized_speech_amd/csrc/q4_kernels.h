@@ -22,6 +22,11 @@ size_t lmhead_workspace_bytes(int64_t M);
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s);
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
+// M <= 4, K % 64 == 0: pps (pairs of blocks per K split) a multiple of 4
+// when splits > 1; partials [splits][M][N] in P, folded by the caller.
+int matmul_small_per_cu();
+void launch_matmul_small(const uint8_t* w, const float* x, float* y, float* P, int64_t M,
+                         int64_t N, int64_t K, int splits, int pps, hipStream_t s);
 
 hipError_t launch_embed(const uint8_t* table, const int32_t* ids, float* out, int64_t M,
                         int64_t N, int64_t K, hipStream_t s);

@@ -872,7 +872,7 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 }  // namespace
 
 // Kernel and K-split plan for a shape.
-enum MatmulKind { MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
+enum MatmulKind { MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
@@ -890,7 +890,12 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   const int nbp = static_cast<int>(K / 64);
   MatmulKind kind;
   int64_t units, slots, min_st, cap = MAX_SPLITS;
-  if (M <= 16 * SK_MAX_MT) {
+  if (M <= 4) {
+    kind = MM_SMALL;
+    units = (N + 63) / 64;
+    slots = static_cast<int64_t>(matmul_small_per_cu()) * cus;  // one round, never a partial second
+    min_st = 4;
+  } else if (M <= 16 * SK_MAX_MT) {
     kind = MM_SKINNY;
     units = (N + SK_ROWS - 1) / SK_ROWS;
     slots = 2 * static_cast<int64_t>(cus);
@@ -913,7 +918,8 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
   while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
   if (want < 2) return MatmulPlan{kind, 1, nbp};
-  const int per = static_cast<int>((nbp + want - 1) / want);
+  int per = static_cast<int>((nbp + want - 1) / want);
+  if (kind == MM_SMALL) per = (per + 3) & ~3;  // whole 4-pair chunks per split
   return MatmulPlan{kind, (nbp + per - 1) / per, per};  // every split non-empty
 }
 
@@ -947,6 +953,9 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
   const MatmulPlan p = plan_matmul(M, N, K, cus, ws ? ws_bytes : 0);
   float* P = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
   switch (p.kind) {
+    case MM_SMALL:
+      launch_matmul_small(w, x, y, P, M, N, K, p.splits, p.stages, s);
+      break;
     case MM_SKINNY:
       switch ((M + 15) / 16) {
         case 1: launch_skinny<1>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;

@@ -25,7 +25,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -63,20 +62,10 @@ def copies_for(nbytes: int) -> int:
     return max(2, -(-CACHE_DEFEAT_BYTES // nbytes))
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources: ties stored counter figures to this code."""
-    import glob
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "q4_quantized_speech_amd", "csrc", "*"))):
-        with open(p, "rb") as fh:
-            h.update(os.path.basename(p).encode())
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(kernel_key: str):
     """HBM bytes per launch measured with rocprofv3 --pmc, if the summary in
-    profiles/ was taken on the current sources; else None."""
+    profiles/ was taken on the current sources of that kernel; else None."""
+    from q4_quantized_speech_amd.profile_driver import source_hash
     path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
     if not os.path.exists(path):
         return None
@@ -86,7 +75,7 @@ def stored_traffic(kernel_key: str):
             if ":" in line and not line.lstrip().startswith("#"):
                 k, _, v = line.partition(":")
                 vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != kernel_source_hash():
+    if vals.get(f"{kernel_key}.source_hash") != source_hash(kernel_key):
         return None
     v = vals.get(f"{kernel_key}.hbm_bytes_per_launch")
     return float(v) if v else None

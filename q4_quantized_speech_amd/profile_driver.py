@@ -15,8 +15,8 @@ written) whose counter readings calibrate the HBM counters.
 counter files of such a run into HBM bytes per call: the counters (KiB per
 dispatch) of the library's kernels, summed over the dispatches one call makes,
 each scaled by (true bytes / counter reading) of the calibration kernel.  The
-result goes into a key-value file that bench.py reads, tagged with a hash of
-the HIP sources so that stale figures are ignored.
+result goes into a key-value file that bench.py reads, each workload tagged
+with a hash of its kernels' sources so that stale figures are ignored.
 
 ``trace`` summarises a ``rocprofv3 --kernel-trace`` CSV per kernel and grid
 size (the library launches one kernel template for several shapes; the grid
@@ -35,7 +35,6 @@ from __future__ import annotations
 import argparse
 import csv
 import hashlib
-import glob
 import os
 import re
 import sys
@@ -56,12 +55,22 @@ def weight_bytes(n: int, k: int) -> int:
     return n * (k // 32) * 18
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources (same rule as bench.py)."""
+# Sources that define each workload family's kernels: a stored counter
+# figure stays valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "matvec": ("q4_matvec.hip", "q4_device.h"),
+    "lmhead": ("q4_matvec.hip", "q4_device.h"),
+    "matmul": ("q4_matmul.hip", "q4_smallm.hip", "q4_device.h"),
+    "embed": ("q4_embed_quant.hip", "q4_device.h"),
+}
+
+
+def source_hash(workload: str) -> str:
+    """Hash of the HIP sources of the workload's kernels."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "q4_quantized_speech_amd", "csrc", "*"))):
-        with open(p, "rb") as fh:
-            h.update(os.path.basename(p).encode())
+    for name in KERNEL_SOURCES[workload.split("_")[0]]:
+        with open(os.path.join(ROOT, "q4_quantized_speech_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -200,11 +209,10 @@ def _traffic(workload: str, fetch: str, write: str, out: str) -> None:
     read_b = f_kib * 1024.0 * f_fac
     write_b = w_kib * 1024.0 * w_fac
     vals, order = _read_kv(out)
-    h = source_hash()
-    if vals.get("source_hash") != h:  # figures from other sources are stale
-        vals, order = {}, []
+    vals.pop("source_hash", None)  # a single hash for all workloads (older files)
+    order = [k for k in order if k != "source_hash"]
     new = {
-        "source_hash": h,
+        f"{workload}.source_hash": source_hash(workload),
         f"{workload}.fetch_kib_per_call_raw": f"{f_kib:.1f}",
         f"{workload}.write_kib_per_call_raw": f"{w_kib:.1f}",
         f"{workload}.fetch_scale": f"{f_fac:.4f}",
@@ -226,7 +234,7 @@ def _traffic(workload: str, fetch: str, write: str, out: str) -> None:
                  "#   (same with --pmc WRITE_SIZE into <Wr>)\n"
                  "#   python -m q4_quantized_speech_amd.profile_driver traffic W \\\n"
                  "#     --fetch <F>/run_counter_collection.csv --write <Wr>/run_counter_collection.csv\n"
-                 "# source_hash ties the figures to the HIP sources they were taken on.\n")
+                 "# W.source_hash ties W's figures to the sources of its kernels.\n")
         for k in order:
             fh.write(f"{k}: {vals[k]}\n")
     print(f"{workload}: read {read_b / 1e6:.3f} MB (raw {f_kib:.0f} KiB x {f_fac:.3f}), "
@@ -253,8 +261,19 @@ def _trace(path: str, out: str | None) -> None:
             grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
             wg = r.get("Workgroup_Size") or r.get("Workgroup_Size_X", "")
             rows[(_short(r["Kernel_Name"]), grid, wg)].append(ns)
-    lines = [f"{'kernel':58s} {'grid(thr)':>10s} {'wg':>4s} {'calls':>7s} {'avg_us':>9s} "
-             f"{'median_us':>9s} {'min_us':>8s}"]
+    lines = []
+    stats = path.replace("_kernel_trace.csv", "_kernel_stats.csv")
+    if stats != path and os.path.exists(stats):  # rocprofv3 --stats of the same run
+        lines.append("## rocprofv3 --stats (per kernel name)")
+        lines.append(f"{'kernel':58s} {'calls':>7s} {'avg_us':>9s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}")
+        with open(stats, newline="") as fh:
+            for r in csv.DictReader(fh):
+                lines.append(f"{_short(r['Name'])[:58]:58s} {int(r['Calls']):7d} "
+                             f"{float(r['AverageNs']) / 1e3:9.3f} {float(r['MinNs']) / 1e3:8.3f} "
+                             f"{float(r['MaxNs']) / 1e3:8.3f} {float(r['Percentage']):6.2f}")
+        lines.append("## per kernel and grid (from the same trace)")
+    lines.append(f"{'kernel':58s} {'grid(thr)':>10s} {'wg':>4s} {'calls':>7s} {'avg_us':>9s} "
+                 f"{'median_us':>9s} {'min_us':>8s}")
     for (k, g, w), v in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
         v = sorted(v)
         lines.append(f"{k[:58]:58s} {g:>10s} {w:>4s} {len(v):7d} {sum(v) / len(v) / 1e3:9.3f} "

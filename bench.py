@@ -25,6 +25,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import statistics
@@ -195,6 +196,48 @@ def main():
                 "bytes_per_launch": dom_bytes,
                 "launch_us_mean": per_proj[dominant]["us"]}
     rows = {"decode_layer_projections": per_proj}
+
+    # Measured read ceiling: a plain coalesced read kernel (libq4probe.so, not
+    # part of the library) over buffers of the dominant kernel's size rotated
+    # the same way, and over 1 GiB; best of a few grid sizes.
+    probe_path = os.path.join(ROOT, "q4_quantized_speech_amd", "libq4probe.so")
+    probe = ctypes.CDLL(probe_path) if os.path.exists(probe_path) else None
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    if probe is not None:
+        probe.q4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        probe.q4probe_read.restype = ctypes.c_int
+
+    def read_ceiling(nbytes):
+        r = copies_for(nbytes)
+        bufs = [torch.full((nbytes,), i & 255, dtype=torch.uint8, device="cuda") for i in range(r)]
+        torch.cuda.synchronize()
+        if probe.q4probe_read(bufs[0].data_ptr(), nbytes, 256, sink.data_ptr(), stream.cuda_stream):
+            raise RuntimeError("read probe launch failed")
+        best = None
+        for grid in (512, 1024, 2048, 4096):
+            g = GraphTimer(torch, stream,
+                           lambda i, grid=grid: probe.q4probe_read(bufs[i % r].data_ptr(), nbytes, grid,
+                                                                  sink.data_ptr(), stream.cuda_stream),
+                           r)
+            us = g.time_us(max(4, reps // 2))
+            del g
+            if best is None or us < best[0]:
+                best = (us, grid)
+        del bufs
+        torch.cuda.empty_cache()
+        return {"us": round(best[0], 3), "gbs": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
+                "grid": best[1]}
+
+    if probe is not None:
+        log("read ceiling")
+        ceil_dom = read_ceiling(dom_bytes)
+        ceil_big = read_ceiling(1 << 30)
+        rows["read_ceiling"] = {f"bytes_{dom_bytes}": ceil_dom, "bytes_1073741824": ceil_big}
+        roofline["ceiling_measured_gbs"] = ceil_dom["gbs"]
+        roofline["frac_of_ceiling"] = round(achieved / ceil_dom["gbs"], 4)
+    else:
+        log("libq4probe.so not built: no measured read ceiling")
 
     def timed(fn, n):
         g = GraphTimer(torch, stream, fn, n)

@@ -1,4 +1,5 @@
-"""Compile the HIP (gfx950) and host C++ sources into the in-tree shared library libq4mi.so.
+"""Compile the HIP (gfx950) and host C++ sources into the in-tree shared library libq4mi.so,
+and the benchmark's read-bandwidth probe into libq4probe.so (measurement only).
 
 Run as ``python -m q4_quantized_speech_amd.build`` or through
 ``__graft_entry__.build()``.  Every call recompiles.
@@ -16,6 +17,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4mi.so")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libq4probe.so")
 OBJ = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
@@ -69,9 +72,20 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _link(sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip"))), PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def _link(srcs, lib):
+    objs = [_compile(s) for s in srcs]
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -361,29 +361,29 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Wave-specialised kernel: 128 x 256 tiles, 768 threads, K % 64 == 0.
-// Waves 0-3 only multiply (each a 64 x 128 sub-tile, 4 x 8 MFMA tiles);
-// waves 4-11 only load, convert X and decode W, one stage ahead of them.  The
-// two roles share the SIMDs (one multiplying and two preparing waves each),
-// so the matrix cores and the vector ALUs work at the same time instead of
-// taking turns; each role runs its own loop and both meet at the same
-// barriers (one per stage).
+// Wave-specialised kernel: 128 x 256 tiles, 512
+// threads, K % 64 == 0.  Waves 0-3 multiply, each a 128 x 64 slice (8 x 4
+// MFMA tiles), and decode their own weight fragments from the raw codes in
+// LDS right before use (each weight row is decoded by one wave only); waves
+// 4-7 only load, convert X to binary16 and copy the raw codes, D stages
+// ahead.  LDS holds X in operand order and the raw codes with a row stride of
+// 12 dwords, so that the 64 lanes of a fragment read (16 rows x 4 code
+// dwords) hit 64 distinct banks.  One barrier per stage.
 // ---------------------------------------------------------------------------
 constexpr int WS_BN = 256, WS_D = 4;
-constexpr int WS_CONS = 256, WS_PT = 512, WS_THREADS = WS_CONS + WS_PT;
-constexpr int WS_XU = T_BM * 16 / WS_PT;           // 16-byte X chunks per producer thread: 4
-constexpr int WS_XRS = WS_PT / 16;                 // rows per X load round: 32
-constexpr int WS_WU = WS_BN * 9 / WS_PT;           // full code-dword rounds: 4
-constexpr int WS_WREST = WS_BN * 9 - WS_WU * WS_PT;  // dwords of the last round: 256
-static_assert(WS_XU * WS_XRS == T_BM && WS_WREST == 256, "producer shares");
+constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
+constexpr int WS_XU = T_BM * 16 / WS_PT;       // 16-byte X chunks per producer thread: 8
+constexpr int WS_XRS = WS_PT / 16;             // rows per X load round: 16
+constexpr int WS_WU = WS_BN * 9 / WS_PT;       // code dwords per producer thread: 9
+constexpr int WS_RS = 12;                      // LDS row stride of the raw codes (dwords)
+static_assert(WS_XU * WS_XRS == T_BM && WS_WU * WS_PT == WS_BN * 9, "producer shares");
 
-__global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
-                      float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
-                      int tiles_n, int ntiles, int split_stages) {
+                       float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
+                       int tiles_n, int ntiles, int split_stages) {
   __shared__ f16x8 As[2][2][T_BM / 16][64];   // [buf][block][16-row tile][element]
-  __shared__ f16x8 Bs[2][2][WS_BN / 16][64];
-  __shared__ uint32_t Wraw[2][WS_BN * 9];
+  __shared__ uint32_t Wr[2][WS_BN * WS_RS];   // raw codes, 12 dwords per row
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / ntiles, tile = item % ntiles;
@@ -397,40 +397,42 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   const int wave = tid >> 6;  // wave-uniform role
 
   if (wave < 4) {
-    // ------------------------------ consumer ------------------------------
+    // ------------------------------ multiply ------------------------------
     const int lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x4v acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
     const int ag = lane >> 4;
     const int ae0 = 16 * ag + ((lane & 15) ^ ag);
     const int ae1 = 16 * ag + ((lane & 15) ^ (ag + 4));
+    f32x4v acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    // this lane's weight row in fragment j: 64 wave + 16 j + lane % 16
+    const int wrow = (64 * wave + (lane & 15)) * WS_RS;
     auto compute = [&](int buf) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk) {
-        f16x8 a[4];
+        f16x8 b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t* r = &Wr[buf][wrow + 16 * j * WS_RS];
+          if (bk == 0) {  // scale in bytes 0..1, codes from byte 2
+            b[j] = decode8_f16(shift16(r[ag + 1], r[ag]), r[0] & 0xFFFFu);
+          } else {        // scale in bytes 18..19, codes from byte 20
+            b[j] = decode8_f16(r[5 + ag], r[4] >> 16);
+          }
+        }
         const int ae = bk ? ae1 : ae0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[buf][bk][wm * 4 + i][ae];
+        for (int i = 0; i < 8; ++i) {
+          const f16x8 a = As[buf][bk][i][ae];
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {  // B fragments in two halves (registers)
-          f16x8 b[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) b[j] = Bs[buf][bk][wn * 8 + jh * 4 + j][lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][jh * 4 + j] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][jh * 4 + j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
         }
       }
     };
-    __syncthreads();  // prologue: stage 0 converted, raw codes staged
-    __syncthreads();  // prologue: stage 0 decoded
+    __syncthreads();  // prologue: stage 0 in LDS
     int t = 0;
     for (; t + 2 <= nst; t += 2) {
       compute(0);
@@ -444,23 +446,23 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     }
     float* out = P ? P + static_cast<int64_t>(split) * M * N : Y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + v;
+        const int row = m0 + i * 16 + (lane >> 4) * 4 + v;
         if (row >= M) continue;
         float* yr = out + static_cast<int64_t>(row) * N;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wave * 64 + j * 16 + (lane & 15);
           if (col < N) yr[col] = acc[i][j][v];
         }
       }
     }
   } else {
-    // ------------------------------ producer ------------------------------
-    const int tp = tid - WS_CONS;  // 0 .. 511
-    // X: chunk xj of rows xr + 32 u (one range-checked resource per 32 rows)
+    // ------------------------------- prepare -------------------------------
+    const int tp = tid - WS_CONS;  // 0 .. 255
+    // X: chunk xj of rows xr + 16 u (one range-checked resource per 16 rows)
     const int xj = tp & 15, xr = tp >> 4;
     __amdgpu_buffer_rsrc_t xrs[WS_XU];
 #pragma unroll
@@ -469,115 +471,73 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
                          static_cast<int64_t>(M - m0 - WS_XRS * u) * K * 4);
     const int xvo = xr * K * 4 + xj * 16;
     const int xb = xj >> 3, xh = (xj >> 2) & 1, xg = xj & 3;
-    const int xe = 16 * xg + ((xr & 15) ^ (xg + 4 * xb));
-    // W: flat code dwords f = tp + 512 u (u < 4) and, for tp < 256, 2048 + tp
-    // (row f / 9, dword f % 9); the extra dword is a wave-uniform branch
+    const int xe = 16 * xg + (xr ^ (xg + 4 * xb));
+    // W: flat code dwords f = tp + 256 u (row f / 9, dword f % 9)
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + static_cast<int64_t>(n0) * rb,
                                                  static_cast<int64_t>(N - n0) * rb);
-    const bool wextra = tp < WS_WREST;
-    int wvo[WS_WU + 1];
+    int wvo[WS_WU], wlo[WS_WU];
 #pragma unroll
-    for (int u = 0; u <= WS_WU; ++u) {
-      const int f = u < WS_WU ? tp + WS_PT * u : WS_WU * WS_PT + (tp & (WS_WREST - 1));
+    for (int u = 0; u < WS_WU; ++u) {
+      const int f = tp + WS_PT * u;
       wvo[u] = static_cast<int>((f / 9) * rb) + (f % 9) * 4;
+      wlo[u] = (f / 9) * WS_RS + f % 9;
     }
-    // decode item: row tp % 256, block tp / 256 (wave-uniform)
-    const int drow = tp & (WS_BN - 1), dblk = tp >> 8;
 
     f32x4 rx[WS_D][WS_XU];
-    uint32_t rw[WS_D][WS_WU + 1];
-    auto load_x = [&](int t, int slot) {
-      const int so = (s0 + (t < nst ? t : nst - 1)) * 256;
+    uint32_t rw[WS_D][WS_WU];
+    auto load = [&](int t, int slot) {
+      const int st = s0 + (t < nst ? t : nst - 1);
 #pragma unroll
       for (int u = 0; u < WS_XU; ++u)
         rx[slot][u] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, so, 0));
-    };
-    auto load_w = [&](int t, int slot) {
-      const int so = (s0 + (t < nst ? t : nst - 1)) * PAIR_BYTES;
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, st * 256, 0));
 #pragma unroll
       for (int u = 0; u < WS_WU; ++u)
-        rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u], so, 0);
-      if (wextra) rw[slot][WS_WU] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[WS_WU], so, 0);
+        rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u], st * PAIR_BYTES, 0);
     };
-    // ordering guard (see the main kernel): volatile first ops on loaded data
     auto pk_f16 = [](float a, float b) -> uint32_t {
       uint32_t r;
       asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
       return r;
     };
-    auto pin = [](uint32_t v) -> uint32_t {
-      uint32_t r;
-      asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-      return r;
-    };
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    auto store_x = [&](int slot, int buf) {
-      char* base = reinterpret_cast<char*>(&As[buf][xb][xr >> 4][xe]) + 8 * xh;
+    auto store = [&](int slot, int buf) {
+      char* base = reinterpret_cast<char*>(&As[buf][xb][0][xe]) + 8 * xh;
 #pragma unroll
       for (int u = 0; u < WS_XU; ++u) {
         const f32x4 v = rx[slot][u];
         const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
-        *reinterpret_cast<u32x2*>(base + u * 2 * 64 * 16) = h;
+        *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
       }
-    };
-    auto store_w = [&](int slot, int buf) {
 #pragma unroll
-      for (int u = 0; u < WS_WU; ++u) Wraw[buf][tp + WS_PT * u] = pin(rw[slot][u]);
-      if (wextra) Wraw[buf][WS_WU * WS_PT + tp] = pin(rw[slot][WS_WU]);
-    };
-    auto decode = [&](int buf) {
-      const uint32_t* wr = &Wraw[buf][drow * 9 + dblk * 4];
-      uint32_t b[5];
-#pragma unroll
-      for (int t = 0; t < 5; ++t) b[t] = wr[t];
-      if (dblk == 0) {  // wave-uniform: bytes 0..19 = scale, codes from byte 2
-        const uint32_t d = b[0] & 0xFFFFu;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          Bs[buf][0][drow >> 4][(drow & 15) + 16 * g] = decode8_f16(shift16(b[g + 1], b[g]), d);
-      } else {          // bytes 16..35 = 2 bytes of block 0, scale, codes from byte 20
-        const uint32_t d = b[0] >> 16;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          Bs[buf][1][drow >> 4][(drow & 15) + 16 * g] = decode8_f16(b[g + 1], d);
-      }
+      for (int u = 0; u < WS_WU; ++u) Wr[buf][wlo[u]] = rw[slot][u];
     };
 
-#define Q4_PSTEP(I)                                         \
-  do {                                                      \
-    load_x(t + (I) + WS_D, (I) % WS_D);                     \
-    load_w(t + (I) + WS_D + 1, (I) % WS_D);                 \
-    __builtin_amdgcn_sched_barrier(0);                      \
-    decode(((I) + 1) % 2);                                  \
-    store_x(((I) + 1) % WS_D, ((I) + 1) % 2);               \
-    store_w(((I) + 1) % WS_D, (I) % 2);                     \
-    __syncthreads();                                        \
+    // step t: issue the loads of stage t + D into the register set stage t
+    // used; put stage t + 1 into LDS buffer (t + 1) % 2 while the multiplying
+    // waves read buffer t % 2.
+#define Q4_W2STEP(I)                                 \
+  do {                                               \
+    load(t + (I) + WS_D, (I) % WS_D);                \
+    __builtin_amdgcn_sched_barrier(0);               \
+    if (t + (I) + 1 < nst)                           \
+      store(((I) + 1) % WS_D, ((I) + 1) % 2);        \
+    __syncthreads();                                 \
   } while (0)
 
-    load_x(0, 0);
-    load_w(0, 0);
-    load_w(1, 1);
-    store_w(0, 0);
-    store_w(1, 1);
-    store_x(0, 0);
 #pragma unroll
-    for (int i = 1; i < WS_D; ++i) {
-      load_x(i, i);
-      load_w(i + 1, i);
-    }
-    __syncthreads();
-    decode(0);
+    for (int i = 0; i < WS_D; ++i) load(i, i);
+    store(0, 0);
     __syncthreads();
     int t = 0;
     for (; t + 4 <= nst; t += 4) {
-      Q4_PSTEP(0); Q4_PSTEP(1); Q4_PSTEP(2); Q4_PSTEP(3);
+      Q4_W2STEP(0); Q4_W2STEP(1); Q4_W2STEP(2); Q4_W2STEP(3);
     }
     const int rem = nst - t;  // uniform; at most three more steps
-    if (rem > 0) Q4_PSTEP(0);
-    if (rem > 1) Q4_PSTEP(1);
-    if (rem > 2) Q4_PSTEP(2);
-#undef Q4_PSTEP
+    if (rem > 0) Q4_W2STEP(0);
+    if (rem > 1) Q4_W2STEP(1);
+    if (rem > 2) Q4_W2STEP(2);
+#undef Q4_W2STEP
   }
 }
 

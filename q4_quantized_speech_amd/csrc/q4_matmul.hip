@@ -516,7 +516,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     // step t: issue the loads of stage t + D into the register set stage t
     // used; put stage t + 1 into LDS buffer (t + 1) % 2 while the multiplying
     // waves read buffer t % 2.
-#define Q4_W2STEP(I)                                 \
+#define Q4_WSSTEP(I)                                 \
   do {                                               \
     load(t + (I) + WS_D, (I) % WS_D);                \
     __builtin_amdgcn_sched_barrier(0);               \
@@ -531,13 +531,13 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     __syncthreads();
     int t = 0;
     for (; t + 4 <= nst; t += 4) {
-      Q4_W2STEP(0); Q4_W2STEP(1); Q4_W2STEP(2); Q4_W2STEP(3);
+      Q4_WSSTEP(0); Q4_WSSTEP(1); Q4_WSSTEP(2); Q4_WSSTEP(3);
     }
     const int rem = nst - t;  // uniform; at most three more steps
-    if (rem > 0) Q4_W2STEP(0);
-    if (rem > 1) Q4_W2STEP(1);
-    if (rem > 2) Q4_W2STEP(2);
-#undef Q4_W2STEP
+    if (rem > 0) Q4_WSSTEP(0);
+    if (rem > 1) Q4_WSSTEP(1);
+    if (rem > 2) Q4_WSSTEP(2);
+#undef Q4_WSSTEP
   }
 }
 

@@ -110,3 +110,23 @@ def test_python_binding_rejects_bad_tensors():
         q4.q4_shape(torch.zeros((4, 18), dtype=torch.int8))
     with pytest.raises(ValueError):
         q4.matvec(torch.zeros((4, 18), dtype=torch.uint8), torch.zeros(32))  # CPU tensors
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/q4.h compiles as C11 with warnings as errors, and a C program
+    linked against the library runs its query and validation paths."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "abi_smoke")
+    libdir = os.path.dirname(q4.LIB_PATH)
+    cmd = [cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_smoke.c"),
+           "-L", libdir, "-lq4mi", f"-Wl,-rpath,{libdir}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "abi_smoke ok" in r.stdout, (r.stdout, r.stderr)

@@ -118,7 +118,7 @@ class GraphTimer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     steps, warmup = max(1, args.steps), max(0, args.warmup)
 

@@ -865,7 +865,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     kind = MM_WIDE;
     units = ((M + T_BM - 1) / T_BM) * ((N + WS_BN - 1) / WS_BN);
     slots = cus;
-    min_st = 8;
+    min_st = 4;
   } else {
     kind = MM_TILE;
     units = ((M + T_BM - 1) / T_BM) * ((N + 127) / 128);

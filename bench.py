@@ -296,8 +296,9 @@ def main():
     del tables, table
 
     # ---------------- small batches: M = 2 .. 15 over the decoder layer ----------------
-    # q4_matvec re-reads each weight row per row of x (M <= 8); q4_matmul's
-    # skinny kernel reads it once
+    # q4_matvec runs its kernel once per row of x (M <= 8; rows after the
+    # first mostly re-read W from the caches); q4_matmul picks per projection
+    # between that and kernels that read W once
     for m in (2, 4, 8, 15):
         xs = [torch.from_numpy(synth.activations(m, k, synth.seed_for(5, 10 + t))).cuda()
               for t, (_, n, k) in enumerate(synth.DECODER_LAYER)]

@@ -81,9 +81,13 @@ size_t q4_row_bytes(int64_t K);
  *   w_q4 : N rows of Q4_0, N*18*K/32 bytes.
  *   x    : [M, K] float32.    y : [M, N] float32 (written, not accumulated).
  *   1 <= M <= 8, N >= 1, K a positive multiple of 32, N*K < 2^40.
- * Float32 products of the exactly decoded weights with x, float32
- * accumulation.  Tuned for M = 1; rows of x beyond the first re-stream W.
- * Results are deterministic (fixed reduction order).
+ * Float32 products of the exactly decoded, centred codes (q - 8) with x,
+ * float32 accumulation, the block scale applied per block: the error stays
+ * within 1e-4 * sum_k |w_k x_k| + 1e-6 for any finite x (a zero weight adds
+ * exactly nothing).  Tuned for M = 1; each row of x runs its own workgroups,
+ * which re-read W (mostly from the caches when W is small).  Results are
+ * deterministic (fixed reduction order) and a row's result does not depend
+ * on the other rows of x.
  */
 q4_status q4_matvec(const void* w_q4, const float* x, float* y,
                     int64_t M, int64_t N, int64_t K, void* stream);
@@ -105,12 +109,16 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  *             that share a workspace must be ordered.
  * M >= 5: weights and activations are rounded to binary16 (round to nearest
  * even) and multiplied on the matrix cores with float32 accumulation, so |x|
- * must stay below 65504.  M <= 4 (several decode streams): the weights enter
- * the matrix cores exactly (q - 8, block scale applied in float32) and x as
- * two binary16 parts after a per-chunk power-of-two scaling, which meets the
- * q4_matvec bound for any finite x.  Deterministic for a given shape, device
- * and ws_bytes; the split changes the order of the float32 sums, so results
- * for different workspace sizes may differ by rounding.
+ * must stay below 65504.  M <= 4 (several decode streams) meets the q4_matvec
+ * bound for any finite x: either each row of x goes through the q4_matvec
+ * kernel (one row, K % 64 == 32, and weights small enough that the rows'
+ * repeated reads stay in the caches: (M - 1) * N * K * 18/32 bytes up to
+ * 40 MiB, K <= 12288), or the weights are read once and enter the matrix
+ * cores exactly (q - 8, block scale applied in float32) with x as two
+ * binary16 parts after a per-chunk power-of-two scaling.  Deterministic for
+ * a given shape, device and ws_bytes; the split changes the order of the
+ * float32 sums, so results for different workspace sizes may differ by
+ * rounding.
  */
 size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 q4_status q4_matmul(const void* w_q4, const float* x, float* y,

@@ -168,8 +168,9 @@ def matmul_workspace(m: int, n: int, k: int, device) -> torch.Tensor | None:
 
 def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None | bool = True, stream=None):
-    """Y = X deq(W)^T on the matrix cores: binary16 operands and float32
-    accumulation, or for M <= 4 exact weights and a two-part x (q4_matvec's bound).
+    """Y = X deq(W)^T.  M >= 5: on the matrix cores with binary16 operands and
+    float32 accumulation.  M <= 4: q4_matvec's bound, either through the matvec
+    kernel per row of x or with exact weights and a two-part x on the matrix cores.
 
     ``workspace``: a uint8 device tensor for the K split, ``True`` to allocate the
     planned size here, or ``None``/``False`` for no split."""

@@ -41,23 +41,24 @@ __device__ __forceinline__ uint32_t shift16(uint32_t hi, uint32_t lo) {
   return __builtin_amdgcn_alignbit(hi, lo, 16);
 }
 
-// sum_{t<4} (lo nibble of byte t of q) * xl[t] + (hi nibble of byte t) * xh[t]
-// with the codes q in [0, 15] (the -8 offset is applied per block).
-__device__ __forceinline__ float nib_dot4(uint32_t q, f32x4 xl, f32x4 xh, float acc) {
+// sum_{t<4} (lo nibble of byte t of q - 8) * xl[t] + (hi nibble - 8) * xh[t]:
+// the centred codes q - 8 (exact in float32), so the rounding of the sum is
+// relative to sum |w x|.
+__device__ __forceinline__ float nib_dot4_centred(uint32_t q, f32x4 xl, f32x4 xh, float acc) {
   uint32_t lo = q & 0x0F0F0F0Fu;
   uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;
-  // Keep the masked dwords opaque so each weight costs one v_cvt_f32_ubyteN
+  // Keep the masked dwords opaque so each code costs one v_cvt_f32_ubyteN
   // rather than a bit-field extract plus a convert.
   asm("" : "+v"(lo));
   asm("" : "+v"(hi));
-  acc = __builtin_fmaf(ubyte_f<0>(lo), xl.x, acc);
-  acc = __builtin_fmaf(ubyte_f<1>(lo), xl.y, acc);
-  acc = __builtin_fmaf(ubyte_f<2>(lo), xl.z, acc);
-  acc = __builtin_fmaf(ubyte_f<3>(lo), xl.w, acc);
-  acc = __builtin_fmaf(ubyte_f<0>(hi), xh.x, acc);
-  acc = __builtin_fmaf(ubyte_f<1>(hi), xh.y, acc);
-  acc = __builtin_fmaf(ubyte_f<2>(hi), xh.z, acc);
-  acc = __builtin_fmaf(ubyte_f<3>(hi), xh.w, acc);
+  acc = __builtin_fmaf(ubyte_f<0>(lo) - 8.f, xl.x, acc);
+  acc = __builtin_fmaf(ubyte_f<1>(lo) - 8.f, xl.y, acc);
+  acc = __builtin_fmaf(ubyte_f<2>(lo) - 8.f, xl.z, acc);
+  acc = __builtin_fmaf(ubyte_f<3>(lo) - 8.f, xl.w, acc);
+  acc = __builtin_fmaf(ubyte_f<0>(hi) - 8.f, xh.x, acc);
+  acc = __builtin_fmaf(ubyte_f<1>(hi) - 8.f, xh.y, acc);
+  acc = __builtin_fmaf(ubyte_f<2>(hi) - 8.f, xh.z, acc);
+  acc = __builtin_fmaf(ubyte_f<3>(hi) - 8.f, xh.w, acc);
   return acc;
 }
 

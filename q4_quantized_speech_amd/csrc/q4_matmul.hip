@@ -832,20 +832,31 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 }  // namespace
 
 // Kernel and K-split plan for a shape.
-enum MatmulKind { MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
+enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
   int stages;  // stages of 64 per split
 };
 
-// Skinny for prompt-prefix row counts (bound by streaming W); 128 x 256
-// wave-specialised tiles for wide outputs (half the X traffic per flop of
-// 128 x 128); 128 x 128 tiles otherwise.  K is split when the units alone
-// cannot fill every workgroup slot: at least `min_st` stages per split, at
-// most MAX_SPLITS, for the skinny kernel no more partial bytes than weight
+// Up to 4 rows of x (decode streams) keep the float32 accuracy of q4_matvec.
+// The matvec kernel, one set of workgroups per row of x, serves one row, any
+// K % 64 == 32 and the shapes whose repeated weight reads stay in the caches
+// ((M - 1) * weight bytes up to STREAM_REREAD: measured faster there, it has
+// no split and no fold launch); the small-M MFMA kernel, weights read once,
+// the rest.  Skinny for prompt-prefix row counts (bound by streaming W);
+// 128 x 256 wave-specialised tiles for wide outputs (half the X traffic per
+// flop of 128 x 128); 128 x 128 tiles otherwise.  K is split when the units
+// alone cannot fill every workgroup slot: at least `min_st` stages per split,
+// at most MAX_SPLITS, for the skinny kernel no more partial bytes than weight
 // bytes, and never more than the workspace holds.
+constexpr int64_t STREAM_REREAD = int64_t{40} << 20;
 static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+  if (M <= 4) {
+    const int64_t wbytes = N * (K / 32) * 18;
+    if (M == 1 || K % 64 != 0 || (K <= 12288 && (M - 1) * wbytes <= STREAM_REREAD))
+      return MatmulPlan{MM_STREAM, 1, 0};
+  }
   if (K % 64 != 0) return MatmulPlan{MM_SIMPLE, 1, 0};
   const int nbp = static_cast<int>(K / 64);
   MatmulKind kind;
@@ -913,6 +924,8 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
   const MatmulPlan p = plan_matmul(M, N, K, cus, ws ? ws_bytes : 0);
   float* P = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
   switch (p.kind) {
+    case MM_STREAM:
+      return launch_matvec(w, x, y, M, N, K, s);
     case MM_SMALL:
       launch_matmul_small(w, x, y, P, M, N, K, p.splits, p.stages, s);
       break;

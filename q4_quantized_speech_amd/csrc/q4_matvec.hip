@@ -9,8 +9,8 @@
 //    row (576 contiguous bytes per DPP row); the K range is split over
 //    KS = ceil(K / 1024) waves of the workgroup, so every lane owns exactly one
 //    pair column for the whole kernel;
-//  * that lane keeps its 64 x values and the two block sums S_b (sum of x over
-//    block b) in registers.  Each wave reads its 1024-float slice of x once,
+//  * that lane keeps its 64 x values in registers (the high nibbles' x
+//    divided by 16, exact).  Each wave reads its 1024-float slice of x once,
 //    coalesced (16 B per lane per load), and hands every lane its 64 values
 //    through LDS: loading them straight from memory would touch 16 cache
 //    lines per load instruction, which costs more address-unit time at the
@@ -24,12 +24,13 @@
 //    the in-order vmcnt counter lets the next pass's loads fly while the
 //    current one computes; rows are read through a range-checked buffer
 //    resource based at the pass's first row;
-//  * codes are masked into half-words as f16 bit patterns (exact subnormals
-//    q * 2^-24, the high nibbles in place as 16 q against x / 16) and fed to
-//    v_fma_mix, which converts and multiply-adds in one instruction per
-//    weight; the two blocks' chains are interleaved so no FMA waits on the
-//    one before it.  The -8 offset is applied per block:
-//    y += d * (2^24 * sum_j q_j 2^-24 x_j - 8 * S_b);
+//  * codes become centred binary16 values (q - 8, the high nibbles in place
+//    as 16 (q - 8) against x / 16; one mask-and-insert under the exponent of
+//    1024 and one packed add per two codes, exact) fed to v_fma_mix, which
+//    converts and multiply-adds in one instruction per weight; the two
+//    blocks' chains are interleaved so no FMA waits on the one before it.
+//    Per block, y += d * sum_j (q_j - 8) x_j: every rounding is relative to
+//    sum |w x|, whatever the spread of x;
 //  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
 //    sums are then added in LDS in a fixed order (deterministic results);
 //  * workgroups are persistent (a grid-stride loop over row groups), as many
@@ -49,23 +50,31 @@ namespace {
 
 
 // Eight codes of one qs dword against x (low nibbles) and x/16 (high
-// nibbles), for two dwords at once.  Each code is masked into a half-word as
-// the f16 bit pattern q (or 16 q): an exact subnormal, q * 2^-24, which
-// v_fma_mix converts for free, so one instruction per weight instead of a
-// byte convert plus an FMA; the sums come out scaled by 2^-24 (exact).  The
-// two chains are interleaved instruction by instruction: a v_fma_mix right
-// after the one it depends on costs a wait state.
+// nibbles), for two dwords at once.  Each code goes into a half-word under
+// the binary16 exponent of 1024 (0x6400 | n, n the low nibble or 16 times the
+// high one) and one packed binary16 add of -1032 or -1152 leaves q - 8 or
+// 16 (q - 8), exactly; v_fma_mix converts the half-word for free.  The sums
+// are of (q - 8) x terms, so their rounding is relative to sum |w x| (an
+// offset form, sum q x - 8 sum x, would lose that bound when a large x meets
+// a zero weight).  The two chains are interleaved instruction by instruction:
+// a v_fma_mix right after the one it depends on costs a wait state.
+// `magic` is 0x64006400 held in a VGPR (the caller keeps it there), so each
+// mask-and-insert is one v_and_or_b32 (a VOP3 takes at most one scalar
+// constant).
 __device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, f32x4 xl0, f32x4 xh0, float& acc0,
-                                              uint32_t q1, f32x4 xl1, f32x4 xh1, float& acc1) {
+                                              uint32_t q1, f32x4 xl1, f32x4 xh1, float& acc1,
+                                              uint32_t magic) {
+  const f16x2 lo_off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+  const f16x2 hi_off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
   const uint32_t v0 = q0 >> 8, v1 = q1 >> 8;
-  const f16x2 a0 = __builtin_bit_cast(f16x2, q0 & 0x000F000Fu);
-  const f16x2 a1 = __builtin_bit_cast(f16x2, q1 & 0x000F000Fu);
-  const f16x2 b0 = __builtin_bit_cast(f16x2, q0 & 0x00F000F0u);
-  const f16x2 b1 = __builtin_bit_cast(f16x2, q1 & 0x00F000F0u);
-  const f16x2 c0 = __builtin_bit_cast(f16x2, v0 & 0x000F000Fu);
-  const f16x2 c1 = __builtin_bit_cast(f16x2, v1 & 0x000F000Fu);
-  const f16x2 e0 = __builtin_bit_cast(f16x2, v0 & 0x00F000F0u);
-  const f16x2 e1 = __builtin_bit_cast(f16x2, v1 & 0x00F000F0u);
+  const f16x2 a0 = __builtin_bit_cast(f16x2, (q0 & 0x000F000Fu) | magic) + lo_off;
+  const f16x2 a1 = __builtin_bit_cast(f16x2, (q1 & 0x000F000Fu) | magic) + lo_off;
+  const f16x2 b0 = __builtin_bit_cast(f16x2, (q0 & 0x00F000F0u) | magic) + hi_off;
+  const f16x2 b1 = __builtin_bit_cast(f16x2, (q1 & 0x00F000F0u) | magic) + hi_off;
+  const f16x2 c0 = __builtin_bit_cast(f16x2, (v0 & 0x000F000Fu) | magic) + lo_off;
+  const f16x2 c1 = __builtin_bit_cast(f16x2, (v1 & 0x000F000Fu) | magic) + lo_off;
+  const f16x2 e0 = __builtin_bit_cast(f16x2, (v0 & 0x00F000F0u) | magic) + hi_off;
+  const f16x2 e1 = __builtin_bit_cast(f16x2, (v1 & 0x00F000F0u) | magic) + hi_off;
   float s0 = acc0, s1 = acc1;
   s0 = __builtin_fmaf(static_cast<float>(a0.x), xl0.x, s0);
   s1 = __builtin_fmaf(static_cast<float>(a1.x), xl1.x, s1);
@@ -227,15 +236,6 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     const f32x4 v = *reinterpret_cast<const f32x4*>(&xs[ks][j][4 * t]);
     xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
   }
-  float S0 = 0.f, S1 = 0.f;
-  {
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) { a0 += xv[t]; a1 += xv[16 + t]; b0 += xv[32 + t]; b1 += xv[48 + t]; }
-    S0 = a0 + a1;
-    S1 = b0 + b1;
-  }
-  if (!cvalid) S0 = S1 = 0.f;
   // x of the high nibbles, divided by 16 (exact)
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -243,7 +243,9 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     xv[48 + t] *= 0.0625f;
   }
 
-  // sum over this lane's pair for R rows: d0*(sum q x - 8 S0) + d1*(...)
+  uint32_t magic = 0x64006400u;  // binary16 1024 in both halves
+  asm("" : "+v"(magic));
+  // sum over this lane's pair for R rows: d0 * sum (q - 8) x + d1 * (...)
   auto compute = [&](uint32_t (&w)[R][9], float (&acc)[R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -254,12 +256,12 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
         const f32x4 xh0 = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
         const f32x4 xl1 = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
         const f32x4 xh1 = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
-        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0, w[r][5 + t], xl1, xh1, s1);
+        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0, w[r][5 + t], xl1, xh1, s1,
+                      magic);
       }
       const float d0 = cvalid ? half_bits_to_float(w[r][0] & 0xFFFFu) : 0.f;
       const float d1 = cvalid ? half_bits_to_float(w[r][4] >> 16) : 0.f;
-      acc[r] = __builtin_fmaf(d0, __builtin_fmaf(s0, 16777216.f, -8.f * S0), 0.f);
-      acc[r] = __builtin_fmaf(d1, __builtin_fmaf(s1, 16777216.f, -8.f * S1), acc[r]);
+      acc[r] = __builtin_fmaf(d1, s1, d0 * s0);
     }
   };
 
@@ -345,14 +347,10 @@ __global__ __launch_bounds__(256) void matvec_any_kernel(
         uint32_t d16, qs[4];
         load_block_any(W, row * nb + b, d16, qs);
         const f32x4* xb = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(b) * QK);
-        float s = 0.f, S = 0.f;
+        float s = 0.f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const f32x4 xl = xb[t], xh = xb[4 + t];
-          s = nib_dot4(qs[t], xl, xh, s);
-          S += (xl.x + xl.y) + (xl.z + xl.w) + ((xh.x + xh.y) + (xh.z + xh.w));
-        }
-        acc = __builtin_fmaf(half_bits_to_float(d16), __builtin_fmaf(-8.f, S, s), acc);
+        for (int t = 0; t < 4; ++t) s = nib_dot4_centred(qs[t], xb[t], xb[4 + t], s);
+        acc = __builtin_fmaf(half_bits_to_float(d16), s, acc);
       }
     }
     const float v = row16_sum(acc);

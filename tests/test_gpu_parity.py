@@ -156,6 +156,40 @@ def test_matvec_decoder_layer_full(name, n, k):
     assert_within(y, ref, b, *MV, f"decoder {name}")
 
 
+@pytest.mark.parametrize("k", [1280, 1056, 9216])
+@pytest.mark.parametrize("case", ["tiny", "huge", "spread", "outlier_on_zero_weights"])
+def test_matvec_x_spread(case, k):
+    """The bound holds for x far from 1 and for a few huge x meeting zero
+    weights (q = 8): the sums are of (q - 8) x terms, so a large x times a
+    zero weight adds nothing, exactly.  K = 1056 takes the generic kernel."""
+    n = 96
+    w = _rand_w(n, k, 40 + k)
+    g = np.random.Generator(np.random.PCG64(41 + k))
+    x = g.standard_normal((2, k))
+    cols = [3, 77, k // 2 + 5, k - 1]
+    if case == "tiny":
+        x *= 1e-30
+    elif case == "huge":
+        x *= 1e8
+    elif case == "spread":
+        x *= 1e-3
+        x[:, 77] = 1e4
+    else:
+        w[:, cols] = 0.0          # a zero column quantises to code 8 in every row
+        x[:, cols] = 1e7
+    x = x.astype(np.float32)
+    qb = O.quantize_q4_0(w)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    announce(f"matvec x {case} k={k}")
+    y = host(q4.matvec(dev(qb), dev(x)))
+    assert_within(y, ref, b, *MV, f"matvec x {case} k={k}")
+    idx, val = q4.lmhead_argmax(dev(qb), dev(x))
+    idx, val = host(idx), host(val)
+    for i in range(2):
+        assert O.argmax_accepts(ref[i], b[i], int(idx[i])), (case, i)
+        assert abs(val[i] - ref[i, idx[i]]) <= O.MATVEC_REL * b[i, idx[i]] + O.MATVEC_ABS
+
+
 def test_matvec_single_3072():
     qb = weights_q4(3072, 3072, synth.seed_for(0, 0))
     x = synth.activations(1, 3072, synth.seed_for(0, 1))[0]

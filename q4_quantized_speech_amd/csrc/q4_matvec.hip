@@ -166,7 +166,9 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
 }
 
 // Pair kernel: K % 64 == 0, K <= 12288, KS = ceil(K / 1024) waves per workgroup.
-template <int KS, bool ARGMAX, int R>
+// XL: x stays in LDS and is read every pass (56 VGPRs at R = 1: 8 waves per
+// SIMD) instead of living in 64 registers per lane (4 waves per SIMD).
+template <int KS, bool ARGMAX, int R, bool XL>
 __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
@@ -209,8 +211,9 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
   };
   // x first (coalesced: the wave's 1024-float slice, 16 B per lane per load),
   // then the weights of the first two passes, so that waiting for x does not
-  // wait for the weights; x goes to this lane's registers through LDS (rows of
-  // 64 floats padded to 68 so the 16 lanes of a DPP row hit distinct banks).
+  // wait for the weights; x goes to LDS (kept there, or copied to this lane's
+  // registers), in rows of 64 floats padded to 68 so the 16 lanes of a DPP
+  // row hit distinct banks.
   __shared__ float xs[KS][16][68];
   f32x4 xg[4];
   {
@@ -224,44 +227,67 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
   }
   load(row0, wa);
   load(row0 + stride, wb);
+  // x of the high nibbles is divided by 16 (exact) on the way in
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = u * 64 + (tid & 63);
-    *reinterpret_cast<f32x4*>(&xs[ks][p >> 4][(p & 15) * 4]) = xg[u];
+    f32x4 v = xg[u];
+    if (p & 4) v *= 0.0625f;
+    *reinterpret_cast<f32x4*>(&xs[ks][p >> 4][(p & 15) * 4]) = v;
   }
   __syncthreads();
-  float xv[64];
+  const float* xr = &xs[ks][j][0];
+  float xv[XL ? 1 : 64];
+  if constexpr (!XL) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(&xs[ks][j][4 * t]);
-    xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
+    for (int t = 0; t < 16; ++t) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * t);
+      xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
+    }
   }
-  // x of the high nibbles, divided by 16 (exact)
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    xv[16 + t] *= 0.0625f;
-    xv[48 + t] *= 0.0625f;
-  }
+  // the 16 x values of step t: low and high nibbles of the two blocks
+  auto xstep = [&](int t, int xo, f32x4& xl0, f32x4& xh0, f32x4& xl1, f32x4& xh1) {
+    if constexpr (XL) {
+      xl0 = *reinterpret_cast<const f32x4*>(xr + xo + 4 * t);
+      xh0 = *reinterpret_cast<const f32x4*>(xr + xo + 16 + 4 * t);
+      xl1 = *reinterpret_cast<const f32x4*>(xr + xo + 32 + 4 * t);
+      xh1 = *reinterpret_cast<const f32x4*>(xr + xo + 48 + 4 * t);
+    } else {
+      xl0 = f32x4{xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
+      xh0 = f32x4{xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
+      xl1 = f32x4{xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
+      xh1 = f32x4{xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
+    }
+  };
 
+  // scale bits of a lane past the last pair forced to +0 (a mask, not a
+  // branch: a branch here lets the compiler split the rows of a pass apart)
+  const uint32_t dmask = cvalid ? 0xFFFFu : 0u;
   uint32_t magic = 0x64006400u;  // binary16 1024 in both halves
   asm("" : "+v"(magic));
   // sum over this lane's pair for R rows: d0 * sum (q - 8) x + d1 * (...)
   auto compute = [&](uint32_t (&w)[R][9], float (&acc)[R]) {
+    int xo = 0;  // opaque per pass, so the LDS reads of x stay in the pass
+    if constexpr (XL) asm volatile("" : "+v"(xo));
+    float s0[R], s1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 xl0, xh0, xl1, xh1;
+      xstep(t, xo, xl0, xh0, xl1, xh1);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0[r], w[r][5 + t], xl1, xh1,
+                      s1[r], magic);
+      // one step's x live at a time
+      if constexpr (XL) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4 xl0 = {xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
-        const f32x4 xh0 = {xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
-        const f32x4 xl1 = {xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
-        const f32x4 xh1 = {xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
-        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0, w[r][5 + t], xl1, xh1, s1,
-                      magic);
-      }
-      const float d0 = cvalid ? half_bits_to_float(w[r][0] & 0xFFFFu) : 0.f;
-      const float d1 = cvalid ? half_bits_to_float(w[r][4] >> 16) : 0.f;
-      acc[r] = __builtin_fmaf(d1, s1, d0 * s0);
+      const float d0 = half_bits_to_float(w[r][0] & dmask);
+      const float d1 = half_bits_to_float((w[r][4] >> 16) & dmask);
+      acc[r] = __builtin_fmaf(d1, s1[r], d0 * s0[r]);
     }
   };
 
@@ -372,12 +398,12 @@ struct PairGrid {
   int64_t g;         // workgroups
   int64_t cu_rows;   // rows handled by the busiest CU
 };
-template <int KS, bool ARGMAX, int R>
+template <int KS, bool ARGMAX, int R, bool XL>
 PairGrid pair_grid(int64_t N) {
   static int per_cu = 0;  // per process; the kernel's resource use is fixed
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL>,
                                                       64 * KS, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -390,22 +416,35 @@ PairGrid pair_grid(int64_t N) {
   return PairGrid{g, ((g + cus - 1) / cus) * rounds * 4 * R};
 }
 
-// Two rows per lane amortise the per-pass reductions and the per-workgroup
-// start-up (each workgroup loads its x slices); one row per lane halves the
-// pass granularity.  Use one row only where two would leave CUs idle and one
-// gives the busiest CU fewer rows.
+// Rows up to 4096 long (KS <= 4), plain products: x in LDS, one row per lane
+// and pass, 8 waves per SIMD -- measured 3-12 % faster than x in registers on
+// the decoder shapes and the 131072-row matvec.  Longer rows keep x in
+// registers (each workgroup stages x once and runs few passes), and so does
+// the argmax (twice the workgroups would double its atomic folds).  There,
+// two rows per lane amortise the per-pass reductions and the per-workgroup
+// start-up; one row per lane halves the pass granularity and is used only
+// where two would leave CUs idle and one gives the busiest CU fewer rows.
 template <int KS, bool ARGMAX>
 void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
                      int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const PairGrid g2 = pair_grid<KS, ARGMAX, 2>(N);
-  const PairGrid g1 = pair_grid<KS, ARGMAX, 1>(N);
-  if (g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows) {
-    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1>), dim3(static_cast<unsigned>(g1.g), M),
-                       dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
-    return;
+  if constexpr (KS <= 4 && !ARGMAX) {
+    const PairGrid g = pair_grid<KS, ARGMAX, 1, true>(N);
+    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true>),
+                       dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS), 0, s, w, x, y, idx, val,
+                       ws, N, static_cast<int>(K));
+  } else {
+    const PairGrid g2 = pair_grid<KS, ARGMAX, 2, false>(N);
+    const PairGrid g1 = pair_grid<KS, ARGMAX, 1, false>(N);
+    const bool one = g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows;
+    if (one)
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, false>),
+                         dim3(static_cast<unsigned>(g1.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
+                         val, ws, N, static_cast<int>(K));
+    else
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2, false>),
+                         dim3(static_cast<unsigned>(g2.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
+                         val, ws, N, static_cast<int>(K));
   }
-  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2>), dim3(static_cast<unsigned>(g2.g), M),
-                     dim3(64 * KS), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K));
 }
 
 template <bool ARGMAX>

@@ -344,26 +344,6 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
   // 16 x 16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + v.
   // With a split, partial sums go to slice `split` of P ([splits][M][N]).
   float* out = P ? P + static_cast<int64_t>(split) * M * N : Y;
-  if (n0 + BN <= N) {
-    // whole columns: range-checked stores drop the rows past M, no branches
-    const int rows = min(M - m0, T_BM);
-    const __amdgpu_buffer_rsrc_t yrs =
-        make_rsrc(out + static_cast<int64_t>(m0) * N, static_cast<int64_t>(rows) * N * 4);
-    const int cb = (n0 + wn * 64 + (lane & 15)) * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ro = (wm * 64 + i * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float val = acc[i][j][v];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0, 0);
-        }
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll

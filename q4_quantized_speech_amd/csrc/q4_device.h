@@ -80,13 +80,15 @@ __device__ __forceinline__ float dpp_f32(float v) {
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
-// row receives the total.  quad_perm swaps lanes within quads, then two row
-// rotations fold the four quad sums.  The add order is the same in every row.
+// row receives the same bits.  Each step adds a lane's partner from a
+// symmetric pairing (swap within pairs, within quads, mirror within half
+// rows, mirror within the row), so two partners add the same two values and
+// get the same result.  The add order is the same in every row.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f32<0x124>(v);  // row_ror:4
-  v += dpp_f32<0x128>(v);  // row_ror:8
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
   return v;
 }
 

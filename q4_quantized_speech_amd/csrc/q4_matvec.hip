@@ -293,26 +293,35 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
 
   float bv = 0.f;
   int bi = -1;
-  // reduce the pass at r0: DPP row sums, then the KS waves in LDS (buffer q)
+  // Reduce the pass at r0 without branches: every lane of a DPP row holds the
+  // row's sum (same bits) and writes it (same value, same address), every
+  // wave adds the KS partial sums (LDS buffer q), then wave 0 consumes them:
+  // a store through a resource covering this pass's rows of Y, with an
+  // out-of-range offset for all lanes but one per row, or the argmax update
+  // as selects.
   auto finish = [&](int64_t r0, float (&acc)[R], int q) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = row16_sum(acc[r]);
-    if constexpr (!ARGMAX) {
-      // Without branches: every lane of a DPP row holds its sum and writes it
-      // (same value, same address), every wave adds the KS partial sums, and
-      // the store goes through a resource covering this pass's rows of Y,
-      // with an out-of-range offset for all lanes but one per row.
-      if constexpr (KS > 1) {
+    if constexpr (KS > 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) red[q][ks][grp * R + r] = acc[r];
-        __syncthreads();
+      for (int r = 0; r < R; ++r) red[q][ks][grp * R + r] = acc[r];
+      __syncthreads();
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float sum = red[q][0][grp * R + r];
-          for (int u = 1; u < KS; ++u) sum += red[q][u][grp * R + r];
-          acc[r] = sum;
-        }
+      for (int r = 0; r < R; ++r) {
+        float sum = red[q][0][grp * R + r];
+        for (int u = 1; u < KS; ++u) sum += red[q][u][grp * R + r];
+        acc[r] = sum;
       }
+    }
+    if constexpr (ARGMAX) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = static_cast<int>(r0) + grp * R + r;
+        const bool take = ks == 0 && row < N && am_better(acc[r], row, bv, bi);
+        bv = take ? acc[r] : bv;
+        bi = take ? row : bi;
+      }
+    } else {
       const int64_t left = N - r0;  // >= 1
       const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
           Y + static_cast<int64_t>(m) * N + r0, 0, static_cast<int>((left < ROWS ? left : ROWS) * 4),
@@ -323,36 +332,6 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
         const float val = acc[r];
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ys,
                                               writer ? (grp * R + r) * 4 : 0x40000000, 0, 0);
-      }
-      return;
-    }
-    if constexpr (KS > 1) {
-      if (j == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) red[q][ks][grp * R + r] = acc[r];
-      }
-      __syncthreads();
-      if (ks == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float sum = red[q][0][grp * R + r];
-          for (int u = 1; u < KS; ++u) sum += red[q][u][grp * R + r];
-          acc[r] = sum;
-        }
-      }
-    }
-    if (ks == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t row = r0 + grp * R + r;
-        if constexpr (ARGMAX) {
-          if (row < N && am_better(acc[r], static_cast<int>(row), bv, bi)) {
-            bv = acc[r];
-            bi = static_cast<int>(row);
-          }
-        } else {
-          if (row < N && j == 0) Y[static_cast<int64_t>(m) * N + row] = acc[r];
-        }
       }
     }
   };

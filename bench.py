@@ -240,8 +240,10 @@ def main():
         log("libq4probe.so not built: no measured read ceiling")
 
     def timed(fn, n):
+        # at least ~400 untimed launches first: replays over freshly cloned
+        # weight copies (the LM head's 1.1 GB above all) run slow for a while
         g = GraphTimer(torch, stream, fn, n)
-        us = g.time_us(max(3, 200 // n))
+        us = g.time_us(max(3, 200 // n), warmup=max(10, 400 // n))
         del g
         return us
 

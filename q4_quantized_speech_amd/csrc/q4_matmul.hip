@@ -566,76 +566,101 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 // prompt prefix (16 / 38 / 76 tokens) is far below a 128-row tile, and the
 // product is bound by streaming W; so W is the MFMA A operand (16 weight rows
 // per wave, decoded straight into operand registers) and X^T the B operand,
-// shared by the 8 waves of a workgroup (128 weight rows) through LDS.  Per
-// stage of 64 k the workgroup stages the raw codes of its 128 rows and the
-// binary16 X^T of the stage (coalesced loads, a ring of SK_D register sets),
-// then every wave decodes its rows and multiplies against all MT tiles of X.
+// shared by the 8 waves of a workgroup (128 weight rows) through LDS.  A
+// stage is SK_PP block pairs: the workgroup stages the raw codes of its 128
+// rows and the binary16 X^T of the stage (coalesced loads, a ring of SK_D
+// register sets), then every wave decodes its rows and multiplies against all
+// MT tiles of X; one barrier per stage.  Up to 32 rows of X a stage is 4
+// pairs (256 k): stages of one pair were bound by the per-stage chain (LDS
+// store, barrier, LDS read, decode, MFMA); beyond that, 4 pairs of X^T would
+// leave one workgroup per CU, so a stage is 1 pair with a deeper ring.  The
+// last stage of a row may be partial; its missing pairs are skipped (all
+// their loads are range-checked).
 // Output lane layout of the 16 x 16 tile: C[n][m] with m = lane % 16 and
 // n = 4 (lane / 16) + v, so each lane writes 4 consecutive columns of Y.
 // ---------------------------------------------------------------------------
-constexpr int SK_ROWS = 128, SK_THREADS = 512, SK_D = 4;
-constexpr int SK_WDW = SK_ROWS * 9;                               // code dwords per stage: 1152
-constexpr int SK_WU = (SK_WDW + SK_THREADS - 1) / SK_THREADS;     // rounds: 3
+constexpr int SK_ROWS = 128, SK_THREADS = 512;
 constexpr int SK_MAX_MT = 5;
+// Block pairs per stage and depth of the load ring: 4 pairs and 2 sets up to
+// 32 rows of X; beyond that the binary16 X^T of 4 pairs would leave one
+// workgroup per CU (LDS), so 1 pair and 4 sets.
+constexpr int sk_pp(int mt) { return mt <= 2 ? 4 : 1; }
+constexpr int sk_d(int mt) { return mt <= 2 ? 2 : 4; }
 
 template <int MT>
 __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     float* __restrict__ P, int M, int N, int K, int groups, int split_stages) {
-  constexpr int XU = (MT * 256 + SK_THREADS - 1) / SK_THREADS;  // 16-byte X chunks per thread
-  __shared__ f16x8 Xs[2][2][MT][64];  // [buf][block][m tile][element]
+  constexpr int SK_PP = sk_pp(MT), SK_D = sk_d(MT);
+  constexpr int SK_RD = SK_PP * 9;                          // code dwords per row and stage
+  constexpr int SK_WDW = SK_ROWS * SK_RD;                   // code dwords per stage
+  constexpr int SK_WU = (SK_WDW + SK_THREADS - 1) / SK_THREADS;
+  constexpr bool WFULL = SK_WU * SK_THREADS == SK_WDW;      // else the last round is partial
+  constexpr int XC = MT * 16 * 16 * SK_PP;                  // 16-byte X chunks per stage
+  constexpr int XU = (XC + SK_THREADS - 1) / SK_THREADS;    // per thread
+  __shared__ f16x8 Xs[2][SK_PP][2][MT][64];      // [buf][pair][block][m tile][element]
   __shared__ uint32_t Wraw[2][SK_WDW];
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / groups, grp = item % groups;
   const int n0 = grp * SK_ROWS;
   const int nbp = K >> 6;
+  const int nss = (nbp + SK_PP - 1) / SK_PP;    // stages in a row
   const int s0 = split * split_stages;
-  const int nst = min(nbp - s0, split_stages);  // >= 1 (host guarantees)
+  const int nst = min(nss - s0, split_stages);  // >= 1 (host guarantees)
   const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // X staging: chunk c = tid + 512 u (row c / 16, 16-byte chunk c % 16);
-  // rows past M read as zeros.  Same operand order and swizzle as the tile
-  // kernels: slot g of row r (block b) at element 16 g + (r % 16 ^ (g + 4 b)).
+  // X staging: chunk c = tid + 512 u, q = c / 16: pair q / (16 MT), m tile
+  // (q / 16) % MT, row in the tile spread so that the 4 rows of one wave's
+  // store are one quad apart (its 8-byte destinations then hit every LDS
+  // bank twice); 16-byte slot c % 16 of the pair.  Same operand order and
+  // swizzle as the tile kernels: slot g of row r (block b) at element
+  // 16 g + (r % 16 ^ (g + 4 b)).  Rows past M read as zeros.
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, static_cast<int64_t>(M) * K * 4);
   int xvo[XU], xlds[XU];
   bool xon[XU];
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int c = tid + SK_THREADS * u;
-    const int r = c >> 4, j = c & 15;
-    const int xb = j >> 3, xh = (j >> 2) & 1, xg = j & 3;
-    xon[u] = c < MT * 256;  // wave-uniform
-    xvo[u] = r * K * 4 + j * 16;
-    xlds[u] = ((xb * MT + (r >> 4)) * 64 + 16 * xg + ((r & 15) ^ (xg + 4 * xb))) * 16 + 8 * xh;
+    xon[u] = c < XC;  // wave-uniform
+    const int q = c >> 4, jj = c & 15, qq = q & 15;
+    const int mt = (q >> 4) % MT, pr = (q >> 4) / MT;
+    const int rl = ((qq & 3) << 2) | (qq >> 2);
+    const int r = 16 * mt + rl;
+    const int xb = jj >> 3, xh = (jj >> 2) & 1, xg = jj & 3;
+    xvo[u] = r * K * 4 + (16 * pr + jj) * 16;
+    xlds[u] = (((pr * 2 + xb) * MT + mt) * 64 + 16 * xg + (rl ^ (xg + 4 * xb))) * 16 + 8 * xh;
   }
-  // W staging: flat code dword f = tid + 512 u of the stage (row f / 9)
+  // W staging: flat code dword f = tid + 512 u of the stage (row f / SK_RD,
+  // dword f % SK_RD of the row's SK_PP pairs, contiguous in memory)
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + static_cast<int64_t>(n0) * rb,
                                                static_cast<int64_t>(N - n0) * rb);
   int wvo[SK_WU];
 #pragma unroll
   for (int u = 0; u < SK_WU; ++u) {
     const int f = tid + SK_THREADS * u;
-    wvo[u] = static_cast<int>((f / 9) * rb) + (f % 9) * 4;
+    wvo[u] = static_cast<int>((f / SK_RD) * rb) + (f % SK_RD) * 4;
   }
-  const bool wlast = tid < SK_WDW - (SK_WU - 1) * SK_THREADS;  // wave-uniform
+  const bool wlast = WFULL || tid < SK_WDW - (SK_WU - 1) * SK_THREADS;  // wave-uniform
 
   f32x4 rx[SK_D][XU];
   uint32_t rw[SK_D][SK_WU];
+  // the stage offset goes into the range-checked vector offset: a partial
+  // last stage reads past its row, and past the buffer for the last row
   auto load = [&](int t, int slot) {
     const int st = s0 + (t < nst ? t : nst - 1);
 #pragma unroll
     for (int u = 0; u < XU; ++u)
       if (xon[u])
         rx[slot][u] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[u], st * 256, 0));
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[u] + st * (SK_PP * 256), 0, 0));
 #pragma unroll
     for (int u = 0; u < SK_WU - 1; ++u)
-      rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u], st * PAIR_BYTES, 0);
+      rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u] + st * (SK_PP * PAIR_BYTES), 0, 0);
     if (wlast)
-      rw[slot][SK_WU - 1] =
-          __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[SK_WU - 1], st * PAIR_BYTES, 0);
+      rw[slot][SK_WU - 1] = __builtin_amdgcn_raw_buffer_load_b32(
+          wrs, wvo[SK_WU - 1] + st * (SK_PP * PAIR_BYTES), 0, 0);
   };
   // ordering guard (see the tile kernels): volatile first ops on loaded data
   auto pk_f16 = [](float a, float b) -> uint32_t {
@@ -655,41 +680,51 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
       if (xon[u]) {
         const f32x4 v = rx[slot][u];
         const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
-        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(&Xs[buf][0][0][0]) + xlds[u]) = h;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(&Xs[buf][0][0][0][0]) + xlds[u]) = h;
       }
 #pragma unroll
     for (int u = 0; u < SK_WU - 1; ++u) Wraw[buf][tid + SK_THREADS * u] = pin(rw[slot][u]);
     if (wlast) Wraw[buf][tid + SK_THREADS * (SK_WU - 1)] = pin(rw[slot][SK_WU - 1]);
   };
 
-  // this wave's rows: n0 + 16 wave + lane % 16; lane group g = lane / 16
+  // this wave's rows: n0 + 16 wave + lane % 16; lane group g = lane / 16.
+  // Even and odd pairs accumulate separately (two MFMA chains).
   const int nl = lane & 15, g = lane >> 4;
-  const int wbase = (16 * wave + nl) * 9;
+  const int wbase = (16 * wave + nl) * SK_RD;
   const int xe0 = 16 * g + (nl ^ g), xe1 = 16 * g + (nl ^ (g + 4));
-  f32x4v acc[MT];
+  f32x4v acc[2][MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
+  for (int i = 0; i < MT; ++i) acc[0][i] = acc[1][i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, int t) {
+    const int pv = min(SK_PP, nbp - (s0 + t) * SK_PP);  // pairs present (uniform)
     const uint32_t* wr = &Wraw[buf][wbase];
-    const uint32_t q0a = wr[g], q0b = wr[g + 1], d01 = wr[0], d1w = wr[4], q1 = wr[5 + g];
-    const f16x8 a0 = decode8_f16(shift16(q0b, q0a), d01 & 0xFFFFu);
-    const f16x8 a1 = decode8_f16(q1, d1w >> 16);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Xs[buf][0][i][xe0], acc[i], 0, 0, 0);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Xs[buf][1][i][xe1], acc[i], 0, 0, 0);
+    for (int p = 0; p < SK_PP; ++p) {
+      if (p < pv) {
+        const uint32_t* w9 = wr + 9 * p;
+        const uint32_t q0a = w9[g], q0b = w9[g + 1], d01 = w9[0], d1w = w9[4], q1 = w9[5 + g];
+        const f16x8 a0 = decode8_f16(shift16(q0b, q0a), d01 & 0xFFFFu);
+        const f16x8 a1 = decode8_f16(q1, d1w >> 16);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          acc[p & 1][i] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Xs[buf][p][0][i][xe0], acc[p & 1][i], 0, 0, 0);
+          acc[p & 1][i] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Xs[buf][p][1][i][xe1], acc[p & 1][i], 0, 0, 0);
+        }
+      }
     }
   };
 
-  // Step t: issue the loads of stage t + D; stage t + 1 (loaded D - 1 steps
-  // ago) into LDS buffer (t + 1) % 2; multiply stage t from buffer t % 2;
-  // barrier.
+  // Step t: issue the loads of stage t + D into the register set stage t
+  // used; stage t + 1 (loaded D - 1 steps ago) into LDS buffer (t + 1) % 2;
+  // multiply stage t from buffer t % 2; barrier.
 #define Q4_SSTEP(I)                                         \
   do {                                                      \
     load(t + (I) + SK_D, (I) % SK_D);                       \
     __builtin_amdgcn_sched_barrier(0);                      \
     store(((I) + 1) % SK_D, ((I) + 1) % 2);                 \
-    compute((I) % 2);                                       \
+    compute((I) % 2, t + (I));                              \
     __syncthreads();                                        \
   } while (0)
 
@@ -698,13 +733,21 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
   store(0, 0);
   __syncthreads();
   int t = 0;
-  for (; t + 4 <= nst; t += 4) {
-    Q4_SSTEP(0); Q4_SSTEP(1); Q4_SSTEP(2); Q4_SSTEP(3);
+  if constexpr (SK_D == 2) {
+    for (; t + 2 <= nst; t += 2) {
+      Q4_SSTEP(0); Q4_SSTEP(1);
+    }
+    if (t < nst) Q4_SSTEP(0);
+  } else {
+    static_assert(SK_D == 4, "ring of 2 or 4 register sets");
+    for (; t + 4 <= nst; t += 4) {
+      Q4_SSTEP(0); Q4_SSTEP(1); Q4_SSTEP(2); Q4_SSTEP(3);
+    }
+    const int rem = nst - t;  // uniform; at most three more steps
+    if (rem > 0) Q4_SSTEP(0);
+    if (rem > 1) Q4_SSTEP(1);
+    if (rem > 2) Q4_SSTEP(2);
   }
-  const int rem = nst - t;  // uniform; at most three more steps
-  if (rem > 0) Q4_SSTEP(0);
-  if (rem > 1) Q4_SSTEP(1);
-  if (rem > 2) Q4_SSTEP(2);
 #undef Q4_SSTEP
 
   // Y[m][n] for m = 16 i + lane % 16, n = n0 + 16 wave + 4 (lane / 16) + v
@@ -714,13 +757,14 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
   for (int i = 0; i < MT; ++i) {
     const int m = 16 * i + nl;
     if (m >= M) continue;
+    const f32x4v a = acc[0][i] + acc[1][i];
     float* yr = out + static_cast<int64_t>(m) * N + nb;
     if ((N & 3) == 0 && nb + 4 <= N) {
-      *reinterpret_cast<f32x4v*>(yr) = acc[i];
+      *reinterpret_cast<f32x4v*>(yr) = a;
     } else {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (nb + v < N) yr[v] = acc[i][v];
+        if (nb + v < N) yr[v] = a[v];
     }
   }
 }
@@ -856,7 +900,7 @@ enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
-  int stages;  // stages of 64 per split
+  int stages;  // kernel stages per split (64 k, or 256 k for the skinny kernel up to M = 32)
 };
 
 // Up to 4 rows of x (decode streams) keep the float32 accuracy of q4_matvec.
@@ -890,7 +934,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     kind = MM_SKINNY;
     units = (N + SK_ROWS - 1) / SK_ROWS;
     slots = 2 * static_cast<int64_t>(cus);
-    min_st = 4;
+    min_st = sk_pp(static_cast<int>((M + 15) / 16)) == 1 ? 4 : 1;  // at least 256 k
     cap = std::max<int64_t>(1, (K * 9 / 16) / (4 * M));
   } else if (N >= 512) {
     kind = MM_WIDE;
@@ -903,15 +947,18 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     slots = 2 * static_cast<int64_t>(cus);
     min_st = 8;
   }
+  // stages of the kernel: sk_pp pairs for the skinny kernel, one pair otherwise
+  const int spp = kind == MM_SKINNY ? sk_pp(static_cast<int>((M + 15) / 16)) : 1;
+  const int nstg = (nbp + spp - 1) / spp;
   int64_t want = slots / units;
-  want = std::min<int64_t>(want, nbp / min_st);
+  want = std::min<int64_t>(want, nstg / min_st);
   want = std::min<int64_t>(want, std::min<int64_t>(cap, MAX_SPLITS));
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
   while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
-  if (want < 2) return MatmulPlan{kind, 1, nbp};
-  int per = static_cast<int>((nbp + want - 1) / want);
+  if (want < 2) return MatmulPlan{kind, 1, nstg};
+  int per = static_cast<int>((nstg + want - 1) / want);
   if (kind == MM_SMALL) per = (per + 3) & ~3;  // whole 4-pair chunks per split
-  return MatmulPlan{kind, (nbp + per - 1) / per, per};  // every split non-empty
+  return MatmulPlan{kind, (nstg + per - 1) / per, per};  // every split non-empty
 }
 
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {

@@ -272,12 +272,14 @@ def test_matmul_split_k(m, n, k):
         assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), tag
 
 
-@pytest.mark.parametrize("m", [1, 16, 17, 48, 80, 81])
-@pytest.mark.parametrize("n,k", [(100, 128), (257, 2048), (130, 640)])
+@pytest.mark.parametrize("m", [1, 16, 17, 32, 33, 48, 80, 81])
+@pytest.mark.parametrize("n,k", [(100, 128), (257, 2048), (130, 640), (70, 192), (33, 64)])
 def test_matmul_skinny_edges(m, n, k):
     """Row counts at the skinny kernel's tile edges (16 per MFMA tile, up to
-    80) and just past it (81 goes to the 128-row tiles); ragged N; with the
-    planned workspace (K split where planned) and without one."""
+    80; up to 32 rows a stage is four block pairs, so K of 1, 2, 3, 10 pairs
+    ends in a partial stage) and just past it (81 goes to the 128-row tiles);
+    ragged N; with the planned workspace (K split where planned) and without
+    one."""
     qb = O.quantize_q4_0(_rand_w(n, k, 7 * m + n + k))
     x = _rand_x(m, k, 5 + m)
     ref, b = O.matmul_f64(qb, x, n, k)

@@ -571,27 +571,26 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 // rows and the binary16 X^T of the stage (coalesced loads, a ring of SK_D
 // register sets), then every wave decodes its rows and multiplies against all
 // MT tiles of X; one barrier per stage.  Up to 32 rows of X a stage is 4
-// pairs (256 k): stages of one pair were bound by the per-stage chain (LDS
-// store, barrier, LDS read, decode, MFMA); beyond that, 4 pairs of X^T would
-// leave one workgroup per CU, so a stage is 1 pair with a deeper ring.  The
-// last stage of a row may be partial; its missing pairs are skipped (all
-// their loads are range-checked).
+// pairs (256 k), beyond that 2 (LDS): stages of one pair were bound by the
+// per-stage chain (LDS store, barrier, LDS read, decode, MFMA).  The last
+// stage of a row may be partial; its missing pairs are skipped (all their
+// loads are range-checked).
 // Output lane layout of the 16 x 16 tile: C[n][m] with m = lane % 16 and
 // n = 4 (lane / 16) + v, so each lane writes 4 consecutive columns of Y.
 // ---------------------------------------------------------------------------
 constexpr int SK_ROWS = 128, SK_THREADS = 512;
 constexpr int SK_MAX_MT = 5;
-// Block pairs per stage and depth of the load ring: 4 pairs and 2 sets up to
-// 32 rows of X; beyond that the binary16 X^T of 4 pairs would leave one
-// workgroup per CU (LDS), so 1 pair and 4 sets.
-constexpr int sk_pp(int mt) { return mt <= 2 ? 4 : 1; }
-constexpr int sk_d(int mt) { return mt <= 2 ? 2 : 4; }
+// Block pairs per stage: 4 up to 32 rows of X; beyond that the binary16 X^T
+// of 4 pairs would leave one workgroup per CU (LDS), so 2.  A ring of two
+// register sets.
+constexpr int sk_pp(int mt) { return mt <= 2 ? 4 : 2; }
+constexpr int SK_D = 2;
 
 template <int MT>
 __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     float* __restrict__ P, int M, int N, int K, int groups, int split_stages) {
-  constexpr int SK_PP = sk_pp(MT), SK_D = sk_d(MT);
+  constexpr int SK_PP = sk_pp(MT);
   constexpr int SK_RD = SK_PP * 9;                          // code dwords per row and stage
   constexpr int SK_WDW = SK_ROWS * SK_RD;                   // code dwords per stage
   constexpr int SK_WU = (SK_WDW + SK_THREADS - 1) / SK_THREADS;
@@ -728,26 +727,16 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
     __syncthreads();                                        \
   } while (0)
 
-#pragma unroll
-  for (int i = 0; i < SK_D; ++i) load(i, i);
+  static_assert(SK_D == 2, "the step is unrolled for a ring of two register sets");
+  load(0, 0);
+  load(1, 1);
   store(0, 0);
   __syncthreads();
   int t = 0;
-  if constexpr (SK_D == 2) {
-    for (; t + 2 <= nst; t += 2) {
-      Q4_SSTEP(0); Q4_SSTEP(1);
-    }
-    if (t < nst) Q4_SSTEP(0);
-  } else {
-    static_assert(SK_D == 4, "ring of 2 or 4 register sets");
-    for (; t + 4 <= nst; t += 4) {
-      Q4_SSTEP(0); Q4_SSTEP(1); Q4_SSTEP(2); Q4_SSTEP(3);
-    }
-    const int rem = nst - t;  // uniform; at most three more steps
-    if (rem > 0) Q4_SSTEP(0);
-    if (rem > 1) Q4_SSTEP(1);
-    if (rem > 2) Q4_SSTEP(2);
+  for (; t + 2 <= nst; t += 2) {
+    Q4_SSTEP(0); Q4_SSTEP(1);
   }
+  if (t < nst) Q4_SSTEP(0);
 #undef Q4_SSTEP
 
   // Y[m][n] for m = 16 i + lane % 16, n = n0 + 16 wave + 4 (lane / 16) + v
@@ -900,7 +889,7 @@ enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
-  int stages;  // kernel stages per split (64 k, or 256 k for the skinny kernel up to M = 32)
+  int stages;  // kernel stages per split (64 k; 128 or 256 k for the skinny kernel)
 };
 
 // Up to 4 rows of x (decode streams) keep the float32 accuracy of q4_matvec.
@@ -934,7 +923,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     kind = MM_SKINNY;
     units = (N + SK_ROWS - 1) / SK_ROWS;
     slots = 2 * static_cast<int64_t>(cus);
-    min_st = sk_pp(static_cast<int>((M + 15) / 16)) == 1 ? 4 : 1;  // at least 256 k
+    min_st = 4 / sk_pp(static_cast<int>((M + 15) / 16));  // at least 256 k per split
     cap = std::max<int64_t>(1, (K * 9 / 16) / (4 * M));
   } else if (N >= 512) {
     kind = MM_WIDE;

@@ -445,8 +445,9 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       __syncthreads();
     }
     float* out = P ? P + static_cast<int64_t>(split) * M * N : Y;
-    if (n0 + WS_BN <= N) {
+    if (n0 + WS_BN <= N && N < (1 << 22)) {
       // whole columns: range-checked stores drop the rows past M, no branches
+      // (32-bit offsets: 128 rows of N floats stay below 2^31 bytes)
       const int rows = min(M - m0, T_BM);
       const __amdgpu_buffer_rsrc_t yrs =
           make_rsrc(out + static_cast<int64_t>(m0) * N, static_cast<int64_t>(rows) * N * 4);

@@ -373,6 +373,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline()
+        matmul["cpu_baseline"] = cpu_baseline_matmul(m_enc)
 
     line = {
         "metric": METRIC,
@@ -397,6 +398,44 @@ def main():
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_matmul(m_enc):
+    """The oracle (float64 dequantise + BLAS dgemm, with its error bound) over
+    the encoder layer + adapter at the GPU workload's shapes."""
+    import numpy as np
+
+    from oracle import q4_oracle as O
+    from q4_quantized_speech_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    log("cpu baseline (matmul): encoding the encoder layer with the oracle (untimed)")
+    mats = []
+    for t, (name, n, k) in enumerate(list(synth.ENCODER_LAYER) + [synth.ADAPTER]):
+        m = m_enc // 4 if name == "adapter" else m_enc
+        qb = O.quantize_q4_0(synth.weights(n, k, synth.seed_for(4, t)))
+        x = synth.activations(m, k, synth.seed_for(4, 10 + t))
+        mats.append((qb, x, n, k, m))
+    flop = sum(2.0 * m * n * k for (_, _, n, k, m) in mats)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 and time.perf_counter() - t_start < 25.0:
+        t0 = time.perf_counter()
+        for qb, x, n, k, m in mats:
+            O.matmul_f64(qb, x, n, k)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    log(f"cpu baseline (matmul): {med * 1e3:.1f} ms per encoder layer + adapter")
+    return {"value": round(flop / med / 1e12, 4), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{len(times)} full encoder layers + adapter at M={m_enc} "
+                      f"({flop / 1e9:.1f} GFLOP), median {med * 1e3:.1f} ms; float64 dequantise "
+                      f"(numpy, 1 thread) + dgemm and the |X||W| bound dgemm (BLAS, "
+                      f"{blas_threads} threads)"}
 
 
 def cpu_baseline():

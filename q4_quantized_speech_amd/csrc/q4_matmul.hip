@@ -940,11 +940,35 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   // stages of the kernel: sk_pp pairs for the skinny kernel, one pair otherwise
   const int spp = kind == MM_SKINNY ? sk_pp(static_cast<int>((M + 15) / 16)) : 1;
   const int nstg = (nbp + spp - 1) / spp;
-  int64_t want = slots / units;
-  want = std::min<int64_t>(want, nstg / min_st);
-  want = std::min<int64_t>(want, std::min<int64_t>(cap, MAX_SPLITS));
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
-  while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
+  int64_t want;
+  if (kind == MM_WIDE) {
+    // Estimated time of S splits: the stages of the busiest workgroup slot,
+    // plus (S > 1) the partial slices written and read back by the fold and
+    // the fold's launch.  Measured inputs: ~0.9 us per 128 x 256 x 64 stage,
+    // ~3 TB/s for the partial traffic, ~2 us for the fold launch.  A K
+    // split pays off for few output tiles and long K (the encoder down
+    // projection and the adapter), not for the 1280 x 1280 projection.
+    want = 1;
+    double best = 0.0;
+    const int64_t smax = std::min<int64_t>(MAX_SPLITS, nstg);
+    for (int64_t sp = 1; sp <= smax; ++sp) {
+      if (sp > 1 && static_cast<uint64_t>(sp * slice) > ws_bytes) break;
+      const int64_t per = (nstg + sp - 1) / sp;
+      const int64_t rounds = (units * sp + slots - 1) / slots;
+      double est = 0.9 * static_cast<double>(per * rounds);
+      if (sp > 1) est += 2.0 * static_cast<double>(sp * slice) / 3.0e6 + 2.0;
+      if (sp == 1 || est < best) {
+        best = est;
+        want = sp;
+      }
+    }
+  } else {
+    want = slots / units;
+    want = std::min<int64_t>(want, nstg / min_st);
+    want = std::min<int64_t>(want, std::min<int64_t>(cap, MAX_SPLITS));
+    while (want > 1 && static_cast<uint64_t>(want * slice) > ws_bytes) --want;
+  }
   if (want < 2) return MatmulPlan{kind, 1, nstg};
   int per = static_cast<int>((nstg + want - 1) / want);
   if (kind == MM_SMALL) per = (per + 3) & ~3;  // whole 4-pair chunks per split

@@ -923,7 +923,10 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   } else if (M <= 16 * SK_MAX_MT) {
     kind = MM_SKINNY;
     units = (N + SK_ROWS - 1) / SK_ROWS;
-    slots = 2 * static_cast<int64_t>(cus);
+    // one workgroup per CU, two when the row groups alone fill half the CUs
+    // (measured on the prefix shapes: fewer, longer splits win for N <= 6144,
+    // more workgroups for the 18432-row gate+up)
+    slots = (2 * units > cus ? 2 : 1) * static_cast<int64_t>(cus);
     min_st = 4 / sk_pp(static_cast<int>((M + 15) / 16));  // at least 256 k per split
     cap = std::max<int64_t>(1, (K * 9 / 16) / (4 * M));
   } else if (N >= 512) {

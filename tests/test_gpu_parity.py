@@ -427,6 +427,31 @@ def test_determinism():
     assert host(i1)[0] == host(i2)[0] and host(v1)[0] == host(v2)[0]
 
 
+@pytest.mark.parametrize("op,m,n,k", [
+    ("matvec", 1, 130, 128), ("matvec", 3, 130, 3072), ("matvec", 2, 131, 9216),
+    ("matvec", 1, 5, 4096), ("matmul", 97, 512, 128), ("matmul", 130, 256, 640),
+    ("matmul", 16, 130, 320), ("matmul", 40, 257, 192), ("matmul", 2, 70, 1088)])
+def test_outputs_written_exactly(op, m, n, k):
+    """Every element of Y written and nothing around it: the matvec pair
+    kernel stores through a resource covering a pass's rows (the rows past N
+    of a ragged last pass dropped by its range check), the wide GEMM drops the
+    rows past M the same way, the skinny GEMM ends on a partial stage."""
+    qb = dev(O.quantize_q4_0(_rand_w(n, k, 3 + n)))
+    x = dev(_rand_x(m, k, 4 + m))
+    sentinel = -12345.0
+    pad = 64
+    buf = torch.full((m * n + 2 * pad,), sentinel, dtype=torch.float32, device="cuda")
+    y = buf[pad: pad + m * n].view(m, n)
+    announce(f"outputs written exactly: {op} {m}x{n}x{k}")
+    if op == "matvec":
+        q4.matvec(qb, x, out=y)
+    else:
+        q4.matmul(qb, x, out=y, workspace=None)
+    got = host(buf)
+    assert np.all(got[:pad] == sentinel) and np.all(got[pad + m * n:] == sentinel)
+    assert not np.any(got[pad: pad + m * n] == sentinel)
+
+
 def test_no_write_past_outputs():
     n, k, m = 130, 96, 3
     qb = dev(O.quantize_q4_0(_rand_w(n, k, 1)))

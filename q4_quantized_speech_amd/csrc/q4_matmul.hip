@@ -918,7 +918,11 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   if (M <= 4) {
     kind = MM_SMALL;
     units = (N + 63) / 64;
-    slots = static_cast<int64_t>(matmul_small_per_cu()) * cus;  // one round, never a partial second
+    // one round, never a partial second: all resident workgroups when the
+    // 64-row groups fill half the GPU, else one per CU (fewer, longer splits
+    // measured faster there, as for the skinny kernel)
+    slots = (2 * units > cus ? static_cast<int64_t>(matmul_small_per_cu()) : 1) *
+            static_cast<int64_t>(cus);
     min_st = 4;
   } else if (M <= 16 * SK_MAX_MT) {
     kind = MM_SKINNY;

@@ -372,22 +372,24 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int WS_BN = 256, WS_D = 4;
 constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
-constexpr int WS_XU = T_BM * 16 / WS_PT;       // 16-byte X chunks per producer thread: 8
 constexpr int WS_XRS = WS_PT / 16;             // rows per X load round: 16
 constexpr int WS_WU = WS_BN * 9 / WS_PT;       // code dwords per producer thread: 9
 constexpr int WS_RS = 12;                      // LDS row stride of the raw codes (dwords)
-static_assert(WS_XU * WS_XRS == T_BM && WS_WU * WS_PT == WS_BN * 9, "producer shares");
+static_assert(WS_WU * WS_PT == WS_BN * 9, "producer shares");
 
+template <int BM>
 __global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
                        float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
                        int tiles_n, int ntiles, int split_stages) {
-  __shared__ f16x8 As[2][2][T_BM / 16][64];   // [buf][block][16-row tile][element]
+  constexpr int MI = BM / 16;                 // 16-row tiles of X
+  constexpr int XU = BM * 16 / WS_PT;         // 16-byte X chunks per producer thread
+  __shared__ f16x8 As[2][2][MI][64];          // [buf][block][16-row tile][element]
   __shared__ uint32_t Wr[2][WS_BN * WS_RS];   // raw codes, 12 dwords per row
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / ntiles, tile = item % ntiles;
-  const int m0 = (tile / tiles_n) * T_BM;
+  const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * WS_BN;
   const int nbp = K >> 6;
   const int s0 = split * split_stages;
@@ -402,9 +404,9 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     const int ag = lane >> 4;
     const int ae0 = 16 * ag + ((lane & 15) ^ ag);
     const int ae1 = 16 * ag + ((lane & 15) ^ (ag + 4));
-    f32x4v acc[8][4];
+    f32x4v acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
     // this lane's weight row in fragment j: 64 wave + 16 j + lane % 16
@@ -424,7 +426,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
         }
         const int ae = bk ? ae1 : ae0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < MI; ++i) {
           const f16x8 a = As[buf][bk][i][ae];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -448,12 +450,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     if (n0 + WS_BN <= N && N < (1 << 22)) {
       // whole columns: range-checked stores drop the rows past M, no branches
       // (32-bit offsets: 128 rows of N floats stay below 2^31 bytes)
-      const int rows = min(M - m0, T_BM);
+      const int rows = min(M - m0, BM);
       const __amdgpu_buffer_rsrc_t yrs =
           make_rsrc(out + static_cast<int64_t>(m0) * N, static_cast<int64_t>(rows) * N * 4);
       const int cb = (n0 + wave * 64 + (lane & 15)) * 4;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int ro = (i * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
@@ -466,7 +468,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = m0 + i * 16 + (lane >> 4) * 4 + v;
@@ -485,9 +487,9 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     const int tp = tid - WS_CONS;  // 0 .. 255
     // X: chunk xj of rows xr + 16 u (one range-checked resource per 16 rows)
     const int xj = tp & 15, xr = tp >> 4;
-    __amdgpu_buffer_rsrc_t xrs[WS_XU];
+    __amdgpu_buffer_rsrc_t xrs[XU];
 #pragma unroll
-    for (int u = 0; u < WS_XU; ++u)
+    for (int u = 0; u < XU; ++u)
       xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + WS_XRS * u) * K,
                          static_cast<int64_t>(M - m0 - WS_XRS * u) * K * 4);
     const int xvo = xr * K * 4 + xj * 16;
@@ -504,12 +506,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       wlo[u] = (f / 9) * WS_RS + f % 9;
     }
 
-    f32x4 rx[WS_D][WS_XU];
+    f32x4 rx[WS_D][XU];
     uint32_t rw[WS_D][WS_WU];
     auto load = [&](int t, int slot) {
       const int st = s0 + (t < nst ? t : nst - 1);
 #pragma unroll
-      for (int u = 0; u < WS_XU; ++u)
+      for (int u = 0; u < XU; ++u)
         rx[slot][u] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, st * 256, 0));
 #pragma unroll
@@ -525,7 +527,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     auto store = [&](int slot, int buf) {
       char* base = reinterpret_cast<char*>(&As[buf][xb][0][xe]) + 8 * xh;
 #pragma unroll
-      for (int u = 0; u < WS_XU; ++u) {
+      for (int u = 0; u < XU; ++u) {
         const f32x4 v = rx[slot][u];
         const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
         *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 }  // namespace
 
 // Kernel and K-split plan for a shape.
-enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_TILE, MM_SIMPLE };
+enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_WIDE64, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
@@ -950,24 +952,32 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   const int64_t slice = M * N * static_cast<int64_t>(sizeof(float));
   int64_t want;
   if (kind == MM_WIDE) {
-    // Estimated time of S splits: the stages of the busiest workgroup slot,
-    // plus (S > 1) the partial slices written and read back by the fold and
-    // the fold's launch.  Measured inputs: ~0.9 us per 128 x 256 x 64 stage,
-    // ~3 TB/s for the partial traffic, ~2 us for the fold launch.  A K
-    // split pays off for few output tiles and long K (the encoder down
-    // projection and the adapter), not for the 1280 x 1280 projection.
+    // Estimated time (us) of (M tile, S splits): the stages of the busiest
+    // workgroup slot, plus (S > 1) the partial slices and a fixed cost per
+    // split call.  Fitted to encoder-shape timings: 0.92 us per 128 x 256 x 64
+    // stage, 0.7 us per 64 x 256 x 64 stage, 0.33 us per MB of partial
+    // slices (written, then read back by the fold) and 4 us for the fold's
+    // launch and the shorter pipelines.  The 64-row tile wins where the
+    // 128-row tiles leave CUs idle (the 1280-wide projections, M <= 375);
+    // K is split for few tiles and long K.
     want = 1;
-    double best = 0.0;
+    double best = -1.0;
     const int64_t smax = std::min<int64_t>(MAX_SPLITS, nstg);
-    for (int64_t sp = 1; sp <= smax; ++sp) {
-      if (sp > 1 && static_cast<uint64_t>(sp * slice) > ws_bytes) break;
-      const int64_t per = (nstg + sp - 1) / sp;
-      const int64_t rounds = (units * sp + slots - 1) / slots;
-      double est = 0.9 * static_cast<double>(per * rounds);
-      if (sp > 1) est += 2.0 * static_cast<double>(sp * slice) / 3.0e6 + 2.0;
-      if (sp == 1 || est < best) {
-        best = est;
-        want = sp;
+    const int64_t tn = (N + WS_BN - 1) / WS_BN;
+    const struct { MatmulKind k; int64_t u; double ts; } opt[2] = {
+        {MM_WIDE, ((M + 127) / 128) * tn, 0.92}, {MM_WIDE64, ((M + 63) / 64) * tn, 0.7}};
+    for (const auto& o : opt) {
+      for (int64_t sp = 1; sp <= smax; ++sp) {
+        if (sp > 1 && static_cast<uint64_t>(sp * slice) > ws_bytes) break;
+        const int64_t per = (nstg + sp - 1) / sp;
+        const int64_t rounds = (o.u * sp + slots - 1) / slots;
+        double est = o.ts * static_cast<double>(per * rounds);
+        if (sp > 1) est += 3.3e-7 * static_cast<double>(sp * slice) + 4.0;
+        if (best < 0.0 || est < best) {
+          best = est;
+          want = sp;
+          kind = o.k;
+        }
       }
     }
   } else {
@@ -1026,12 +1036,19 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
         default: launch_skinny<5>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
       }
       break;
-    case MM_WIDE: {
+    case MM_WIDE:
+    case MM_WIDE64: {
+      const int bm = p.kind == MM_WIDE ? 128 : 64;
       const int tiles_n = static_cast<int>((N + WS_BN - 1) / WS_BN);
-      const int ntiles = tiles_n * static_cast<int>((M + T_BM - 1) / T_BM);
-      hipLaunchKernelGGL(matmul_ws_kernel, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s, w, x,
-                         y, P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
-                         tiles_n, ntiles, p.stages);
+      const int ntiles = tiles_n * static_cast<int>((M + bm - 1) / bm);
+      if (p.kind == MM_WIDE)
+        hipLaunchKernelGGL(matmul_ws_kernel<128>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
+                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
+                           static_cast<int>(K), tiles_n, ntiles, p.stages);
+      else
+        hipLaunchKernelGGL(matmul_ws_kernel<64>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
+                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
+                           static_cast<int>(K), tiles_n, ntiles, p.stages);
       break;
     }
     case MM_TILE:

@@ -290,6 +290,23 @@ def test_matmul_skinny_edges(m, n, k):
         assert_within(y, ref, b, *MF, f"skinny {m}x{n}x{k} ws={ws is not None}")
 
 
+@pytest.mark.parametrize("m,n,k", [(81, 512, 128), (100, 1280, 1280), (129, 1300, 640),
+                                   (193, 1280, 5120), (375, 1280, 1280), (93, 3072, 5120),
+                                   (257, 768, 320)])
+def test_matmul_wide_tiles(m, n, k):
+    """The 128 x 256 wave-specialised kernel with 128- or 64-row tiles (the
+    planner picks the tile and the K split per shape): ragged M in both tile
+    heights, ragged N, with the planned workspace and without one."""
+    qb = O.quantize_q4_0(_rand_w(n, k, 11 * m + n + k))
+    x = _rand_x(m, k, 13 + m)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    for ws in (True, None):
+        announce(f"matmul wide {m}x{n}x{k} workspace={ws is not None}")
+        y = host(q4.matmul(wq, xd, workspace=ws))
+        assert_within(y, ref, b, *MF, f"wide {m}x{n}x{k} ws={ws is not None}")
+
+
 def test_matmul_split_k_stays_in_bounds():
     """Partial sums stay inside the workspace, results inside Y."""
     m, n, k = 70, 150, 2048

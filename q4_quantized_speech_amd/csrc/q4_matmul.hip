@@ -361,21 +361,21 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Wave-specialised kernel: 128 x 256 tiles, 512
-// threads, K % 64 == 0.  Waves 0-3 multiply, each a 128 x 64 slice (8 x 4
-// MFMA tiles), and decode their own weight fragments from the raw codes in
-// LDS right before use (each weight row is decoded by one wave only); waves
-// 4-7 only load, convert X to binary16 and copy the raw codes, D stages
-// ahead.  LDS holds X in operand order and the raw codes with a row stride of
-// 12 dwords, so that the 64 lanes of a fragment read (16 rows x 4 code
-// dwords) hit 64 distinct banks.  One barrier per stage.
+// Wave-specialised kernel: BM x 256 tiles (BM = 128 or 64), 512 threads,
+// K % 64 == 0.  Waves 0-3 only multiply, each a BM x 64 slice (BM/16 x 4
+// MFMA tiles), reading both operands from LDS in operand order.  Waves 4-7
+// load a stage D stages ahead (each thread one weight row's 36-byte block
+// pair and 16-byte chunks of X), convert X to binary16 and decode the row's
+// two blocks into binary16 (q - 8) d, once per weight.  One barrier per
+// stage.  Measured on the encoder shapes: decoding in the loading waves and
+// D = 2 ran 2-8 % faster than decoding in the multiplying waves from raw
+// codes in LDS with D = 4 (deeper pipelines were slower still).
 // ---------------------------------------------------------------------------
-constexpr int WS_BN = 256, WS_D = 4;
+constexpr int WS_BN = 256, WS_D = 2;
 constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
 constexpr int WS_XRS = WS_PT / 16;             // rows per X load round: 16
-constexpr int WS_WU = WS_BN * 9 / WS_PT;       // code dwords per producer thread: 9
-constexpr int WS_RS = 12;                      // LDS row stride of the raw codes (dwords)
-static_assert(WS_WU * WS_PT == WS_BN * 9, "producer shares");
+constexpr int WS_WU = 9;                       // code dwords per producer thread: one pair
+static_assert(WS_PT == WS_BN, "one weight row per producer thread");
 
 template <int BM>
 __global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -385,7 +385,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   constexpr int MI = BM / 16;                 // 16-row tiles of X
   constexpr int XU = BM * 16 / WS_PT;         // 16-byte X chunks per producer thread
   __shared__ f16x8 As[2][2][MI][64];          // [buf][block][16-row tile][element]
-  __shared__ uint32_t Wr[2][WS_BN * WS_RS];   // raw codes, 12 dwords per row
+  __shared__ f16x8 Bs[2][2][WS_BN / 16][64];  // [buf][block][16-row fragment][lane]: weights
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / ntiles, tile = item % ntiles;
@@ -409,21 +409,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    // this lane's weight row in fragment j: 64 wave + 16 j + lane % 16
-    const int wrow = (64 * wave + (lane & 15)) * WS_RS;
     auto compute = [&](int buf) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk) {
         f16x8 b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t* r = &Wr[buf][wrow + 16 * j * WS_RS];
-          if (bk == 0) {  // scale in bytes 0..1, codes from byte 2
-            b[j] = decode8_f16(shift16(r[ag + 1], r[ag]), r[0] & 0xFFFFu);
-          } else {        // scale in bytes 18..19, codes from byte 20
-            b[j] = decode8_f16(r[5 + ag], r[4] >> 16);
-          }
-        }
+        for (int j = 0; j < 4; ++j) b[j] = Bs[buf][bk][4 * wave + j][lane];
         const int ae = bk ? ae1 : ae0;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -495,16 +486,10 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     const int xvo = xr * K * 4 + xj * 16;
     const int xb = xj >> 3, xh = (xj >> 2) & 1, xg = xj & 3;
     const int xe = 16 * xg + (xr ^ (xg + 4 * xb));
-    // W: flat code dwords f = tp + 256 u (row f / 9, dword f % 9)
+    // W: this thread's weight row n0 + tp, one 36-byte pair per stage
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + static_cast<int64_t>(n0) * rb,
                                                  static_cast<int64_t>(N - n0) * rb);
-    int wvo[WS_WU], wlo[WS_WU];
-#pragma unroll
-    for (int u = 0; u < WS_WU; ++u) {
-      const int f = tp + WS_PT * u;
-      wvo[u] = static_cast<int>((f / 9) * rb) + (f % 9) * 4;
-      wlo[u] = (f / 9) * WS_RS + f % 9;
-    }
+    const int wvo = static_cast<int>(tp * rb);
 
     f32x4 rx[WS_D][XU];
     uint32_t rw[WS_D][WS_WU];
@@ -514,9 +499,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       for (int u = 0; u < XU; ++u)
         rx[slot][u] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, st * 256, 0));
-#pragma unroll
-      for (int u = 0; u < WS_WU; ++u)
-        rw[slot][u] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wvo[u], st * PAIR_BYTES, 0);
+      const int wo = wvo + st * PAIR_BYTES;
+      const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, 0));
+      const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 16, 0));
+      rw[slot][0] = a.x; rw[slot][1] = a.y; rw[slot][2] = a.z; rw[slot][3] = a.w;
+      rw[slot][4] = b.x; rw[slot][5] = b.y; rw[slot][6] = b.z; rw[slot][7] = b.w;
+      rw[slot][8] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wo, 32, 0);
     };
     auto pk_f16 = [](float a, float b) -> uint32_t {
       uint32_t r;
@@ -532,19 +520,25 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
         const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
         *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
       }
+      // the row's two blocks, decoded once into operand order
+      const uint32_t* c = rw[slot];
+      f16x8* bw = &Bs[buf][0][tp >> 4][tp & 15];
 #pragma unroll
-      for (int u = 0; u < WS_WU; ++u) Wr[buf][wlo[u]] = rw[slot][u];
+      for (int g = 0; g < 4; ++g) bw[16 * g] = decode8_f16(shift16(c[g + 1], c[g]), c[0] & 0xFFFFu);
+      bw = &Bs[buf][1][tp >> 4][tp & 15];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bw[16 * g] = decode8_f16(c[5 + g], c[4] >> 16);
     };
 
     // step t: issue the loads of stage t + D into the register set stage t
     // used; put stage t + 1 into LDS buffer (t + 1) % 2 while the multiplying
-    // waves read buffer t % 2.
+    // waves read buffer t % 2 (stage s lives in register set s % D).
 #define Q4_WSSTEP(I)                                 \
   do {                                               \
     load(t + (I) + WS_D, (I) % WS_D);                \
     __builtin_amdgcn_sched_barrier(0);               \
     if (t + (I) + 1 < nst)                           \
-      store(((I) + 1) % WS_D, ((I) + 1) % 2);        \
+      store(((I) + 1) % WS_D, (t + (I) + 1) & 1);    \
     __syncthreads();                                 \
   } while (0)
 
@@ -553,13 +547,13 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     store(0, 0);
     __syncthreads();
     int t = 0;
-    for (; t + 4 <= nst; t += 4) {
-      Q4_WSSTEP(0); Q4_WSSTEP(1); Q4_WSSTEP(2); Q4_WSSTEP(3);
+    for (; t + WS_D <= nst; t += WS_D) {
+#pragma unroll
+      for (int I = 0; I < WS_D; ++I) Q4_WSSTEP(I);
     }
-    const int rem = nst - t;  // uniform; at most three more steps
-    if (rem > 0) Q4_WSSTEP(0);
-    if (rem > 1) Q4_WSSTEP(1);
-    if (rem > 2) Q4_WSSTEP(2);
+#pragma unroll
+    for (int I = 0; I < WS_D - 1; ++I)
+      if (t + I < nst) Q4_WSSTEP(I);
 #undef Q4_WSSTEP
   }
 }

@@ -96,28 +96,38 @@ __device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, f32x4 xl0, f32x4 xh0,
   acc1 = s1;
 }
 
-// Argmax bookkeeping: idx < 0 means "no candidate"; NaN never wins.
+// Argmax bookkeeping: idx < 0 means "no candidate", which never wins over a
+// candidate, whatever its value; NaN never wins.
 __device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) {
-  if (bi < 0) return !(v != v);
+  if (i < 0 || v != v) return false;
+  if (bi < 0) return true;
   return v > bv || (v == bv && i < bi);
 }
 
 // Fold the candidates of all threads of the workgroup; result valid in thread 0.
+// A butterfly over each wave, then one over the waves' candidates in wave 0:
+// the order of a strict total order's comparisons does not change the winner.
 __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
-  __shared__ float sv[64];
-  __shared__ int si[64];
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, 16);
-    const int oi = __shfl_xor(bi, o, 16);
-    if (am_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  const int grp = threadIdx.x >> 4;
-  if ((threadIdx.x & 15) == 0) { sv[grp] = bv; si[grp] = bi; }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  auto fold = [&](int lanes) {
+    for (int o = lanes >> 1; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, lanes);
+      const int oi = __shfl_xor(bi, o, lanes);
+      const bool t = am_better(ov, oi, bv, bi);
+      bv = t ? ov : bv;
+      bi = t ? oi : bi;
+    }
+  };
+  fold(64);
+  const int w = threadIdx.x >> 6, nw = static_cast<int>((blockDim.x + 63) >> 6);
+  if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int g = 1; g < static_cast<int>(blockDim.x >> 4); ++g)
-      if (am_better(sv[g], si[g], bv, bi)) { bv = sv[g]; bi = si[g]; }
+  if (w == 0) {
+    const int l = threadIdx.x;
+    bv = l < nw ? sv[l] : 0.f;
+    bi = l < nw ? si[l] : -1;
+    fold(16);
   }
 }
 

@@ -393,6 +393,24 @@ def test_lmhead_ties_and_planted():
         assert abs(val[i] - y[idx[i]]) <= O.MATVEC_REL * b[idx[i]] + O.MATVEC_ABS
 
 
+@pytest.mark.parametrize("n,k", [(5000, 3072), (3000, 9216), (700, 96), (40, 256)])
+def test_lmhead_all_logits_negative(n, k):
+    """Every logit below zero: the workgroups' empty slots (no row yet) must
+    never win over a real candidate in the per-workgroup fold."""
+    rng = np.random.default_rng(77 + k)
+    w = -np.abs(rng.standard_normal((n, k))).astype(np.float32) * np.float32(0.02)
+    x = np.abs(rng.standard_normal((2, k))).astype(np.float32) + np.float32(0.1)
+    qb = O.quantize_q4_0(w)
+    announce(f"lmhead all-negative n={n} k={k}")
+    idx, val = q4.lmhead_argmax(dev(qb), dev(x))
+    idx, val = host(idx), host(val)
+    for i in range(2):
+        y, b = O.lmhead_logits(qb, x[i], n, k)
+        assert y.max() < 0.0
+        assert O.argmax_accepts(y, b, int(idx[i])), (i, int(idx[i]), O.argmax_lowest(y))
+        assert abs(val[i] - y[idx[i]]) <= O.MATVEC_REL * b[idx[i]] + O.MATVEC_ABS
+
+
 def test_lmhead_workspace_reuse_and_odd_k():
     """The workspace starts zeroed and every call leaves it zeroed, so calls
     ordered on one stream can share it; K % 64 == 32 takes the generic kernel."""

@@ -178,18 +178,21 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
 // Pair kernel: K % 64 == 0, K <= 12288, KS = ceil(K / 1024) waves per workgroup.
 // XL: x stays in LDS and is read every pass (56 VGPRs at R = 1: 8 waves per
 // SIMD) instead of living in 64 registers per lane (4 waves per SIMD).
-template <int KS, bool ARGMAX, int R, bool XL>
-__global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
+// G row groups of KS waves share the workgroup's x (each group stages a
+// quarter of it when G = 4) and cover 4 R G consecutive rows per pass.
+template <int KS, bool ARGMAX, int R, bool XL, int G>
+__global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
     int K) {
-  constexpr int ROWS = 4 * R;  // rows per pass
+  constexpr int ROWS = 4 * R * G;  // rows per pass
   __shared__ float red[2][KS][ROWS];
   const int m = blockIdx.y;
   const int nbp = K >> 6;
   const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
   const int tid = threadIdx.x;
-  const int ks = tid >> 6, j = tid & 15, grp = (tid >> 4) & 3;
+  const int wv = tid >> 6, ks = wv % KS, gi = wv / KS, j = tid & 15;
+  const int grp = gi * 4 + ((tid >> 4) & 3);  // DPP row of the pass
   const int craw = j + 16 * ks;
   const bool cvalid = craw < nbp;
   const int c = cvalid ? craw : nbp - 1;
@@ -232,7 +235,8 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = (u * 64 + (tid & 63)) * 4;
-      xg[u] = p < lim ? *reinterpret_cast<const f32x4*>(xw + p) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u % G == gi)
+        xg[u] = p < lim ? *reinterpret_cast<const f32x4*>(xw + p) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   load(row0, wa);
@@ -240,6 +244,7 @@ __global__ __launch_bounds__(64 * KS) void matvec_pairs_kernel(
   // x of the high nibbles is divided by 16 (exact) on the way in
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    if (u % G != gi) continue;
     const int p = u * 64 + (tid & 63);
     f32x4 v = xg[u];
     if (p & 4) v *= 0.0625f;
@@ -416,50 +421,63 @@ struct PairGrid {
   int64_t g;         // workgroups
   int64_t cu_rows;   // rows handled by the busiest CU
 };
-template <int KS, bool ARGMAX, int R, bool XL>
+template <int KS, bool ARGMAX, int R, bool XL, int G>
 PairGrid pair_grid(int64_t N) {
   static int per_cu = 0;  // per process; the kernel's resource use is fixed
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL>,
-                                                      64 * KS, 0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL, G>,
+                                                      64 * KS * G, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
   }
   const int64_t cus = device_info().cu_count;
-  const int64_t passes = (N + 4 * R - 1) / (4 * R);
+  const int64_t passes = (N + 4 * R * G - 1) / (4 * R * G);
   const int64_t cap = cus * per_cu;
   const int64_t rounds = (passes + cap - 1) / cap;
   const int64_t g = (passes + rounds - 1) / rounds;
-  return PairGrid{g, ((g + cus - 1) / cus) * rounds * 4 * R};
+  return PairGrid{g, ((g + cus - 1) / cus) * rounds * 4 * R * G};
 }
 
 // Rows up to 4096 long (KS <= 4), plain products: x in LDS, one row per lane
 // and pass, 8 waves per SIMD -- measured 3-12 % faster than x in registers on
-// the decoder shapes and the 131072-row matvec.  Longer rows keep x in
-// registers (each workgroup stages x once and runs few passes), and so does
-// the argmax (twice the workgroups would double its atomic folds).  There,
-// two rows per lane amortise the per-pass reductions and the per-workgroup
+// the decoder shapes.  Tall matrices (the 131072-row LM head, as a matvec or
+// with the argmax) take four row groups per workgroup sharing one copy of x
+// in LDS: a quarter of the workgroups, each pass 16 contiguous rows (-4 % on
+// both; slower on the decoder shapes, where each workgroup runs only a few
+// passes).  Longer rows keep x in registers (each workgroup stages x once and
+// runs few passes), and so does the argmax of shorter tables.  There, two
+// rows per lane amortise the per-pass reductions and the per-workgroup
 // start-up; one row per lane halves the pass granularity and is used only
 // where two would leave CUs idle and one gives the busiest CU fewer rows.
+constexpr int64_t MV_GROUPED_ROWS = 65536;
 template <int KS, bool ARGMAX>
 void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
                      int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if constexpr (KS <= 4) {
+    if (N >= MV_GROUPED_ROWS) {
+      const PairGrid g = pair_grid<KS, ARGMAX, 1, true, 4>(N);
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true, 4>),
+                         dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS * 4), 0, s, w, x, y,
+                         idx, val, ws, N, static_cast<int>(K));
+      return;
+    }
+  }
   if constexpr (KS <= 4 && !ARGMAX) {
-    const PairGrid g = pair_grid<KS, ARGMAX, 1, true>(N);
-    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true>),
+    const PairGrid g = pair_grid<KS, ARGMAX, 1, true, 1>(N);
+    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true, 1>),
                        dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS), 0, s, w, x, y, idx, val,
                        ws, N, static_cast<int>(K));
   } else {
-    const PairGrid g2 = pair_grid<KS, ARGMAX, 2, false>(N);
-    const PairGrid g1 = pair_grid<KS, ARGMAX, 1, false>(N);
+    const PairGrid g2 = pair_grid<KS, ARGMAX, 2, false, 1>(N);
+    const PairGrid g1 = pair_grid<KS, ARGMAX, 1, false, 1>(N);
     const bool one = g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows;
     if (one)
-      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, false>),
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, false, 1>),
                          dim3(static_cast<unsigned>(g1.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
                          val, ws, N, static_cast<int>(K));
     else
-      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2, false>),
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2, false, 1>),
                          dim3(static_cast<unsigned>(g2.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
                          val, ws, N, static_cast<int>(K));
   }

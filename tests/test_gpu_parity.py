@@ -411,6 +411,50 @@ def test_lmhead_all_logits_negative(n, k):
         assert abs(val[i] - y[idx[i]]) <= O.MATVEC_REL * b[idx[i]] + O.MATVEC_ABS
 
 
+def _tall_view(n, k, negative=False):
+    """The first n rows of the LM-head table's bytes read as an n x k Q4_0
+    matrix (any k % 32 == 0 regroups the same 18-byte blocks).  negative:
+    every weight made <= 0 (scale sign set, every code 8..15)."""
+    nbytes = n * (k // 32) * 18
+    b = lm_table().reshape(-1)[:nbytes].copy()
+    if negative:
+        blk = b.reshape(-1, 18)
+        blk[:, 1] |= 0x80
+        blk[:, 2:] |= 0x88
+    return b.reshape(n, (k // 32) * 18)
+
+
+@pytest.mark.parametrize("n,k", [(65549, 1024), (65601, 2048), (70001, 3072), (65536, 4096)])
+def test_tall_matvec_and_argmax(n, k):
+    """Tables of 65536 rows or more take four row groups per workgroup:
+    ragged row counts and every K that keeps x in LDS."""
+    qb = _tall_view(n, k)
+    x = _rand_x(2, k, 900 + k)
+    wq = dev(qb)
+    announce(f"tall matvec/argmax n={n} k={k}")
+    y = host(q4.matvec(wq, dev(x[0])))
+    idx, val = q4.lmhead_argmax(wq, dev(x))
+    idx, val = host(idx), host(val)
+    ref, b = O.lmhead_logits(qb, x[0], n, k)
+    assert_within(y, ref, b, *MV, f"tall matvec n={n} k={k}")
+    for i in range(2):
+        yi, bi = (ref, b) if i == 0 else O.lmhead_logits(qb, x[i], n, k)
+        assert O.argmax_accepts(yi, bi, int(idx[i])), (i, int(idx[i]), O.argmax_lowest(yi))
+        assert abs(val[i] - yi[idx[i]]) <= O.MATVEC_REL * bi[idx[i]] + O.MATVEC_ABS
+
+
+def test_tall_argmax_all_logits_negative():
+    n, k = 70001, 3072
+    qb = _tall_view(n, k, negative=True)
+    x = np.abs(_rand_x(1, k, 4321)) + np.float32(0.1)
+    announce("tall argmax all-negative")
+    idx, val = q4.lmhead_argmax(dev(qb), dev(x))
+    y, b = O.lmhead_logits(qb, x[0], n, k)
+    assert y.max() < 0.0
+    i = int(host(idx)[0])
+    assert O.argmax_accepts(y, b, i), (i, O.argmax_lowest(y))
+
+
 def test_lmhead_workspace_reuse_and_odd_k():
     """The workspace starts zeroed and every call leaves it zeroed, so calls
     ordered on one stream can share it; K % 64 == 32 takes the generic kernel."""

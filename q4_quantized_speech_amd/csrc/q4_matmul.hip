@@ -15,7 +15,15 @@
 // (q - 8) * d in binary16 (exact q - 8, one rounding of the product); X is
 // rounded to binary16 (nearest even); accumulation is float32.
 //
-// Main kernel (K % 64 == 0): a 256-thread workgroup owns a 128 x 128 tile of
+// Kernels, by shape (the planner at the end of this file picks one): the
+// wave-specialised kernel for outputs at least 512 wide (the encoder and the
+// adapter: BM x 256 tiles, loading waves decode, multiplying waves only read
+// LDS), the skinny kernel for 5 to 80 rows of X (prompt prefixes: W streams
+// through the MFMA A operand), the tile kernel below for narrower outputs,
+// the simple kernel for K % 64 == 32; up to 4 rows of X go to the matvec or
+// to the small-M kernel (q4_smallm.hip).
+//
+// Tile kernel (K % 64 == 0): a 256-thread workgroup owns a 128 x 128 tile of
 // Y; each of its four waves a 64 x 64 sub-tile (4 x 4 MFMA tiles).  K
 // advances in stages of 64 (one 36-byte block pair per weight row).  Global
 // loads are coalesced (16 lanes read one row of X; consecutive lanes read
@@ -25,9 +33,9 @@
 // one stage earlier) into LDS in operand order, double buffered, while the
 // loads of later stages are in flight in a ring of three register sets.  73
 // KiB of LDS per workgroup lets two workgroups share a CU.  When the tiles
-// cannot fill the GPU, K is split over several workgroups per tile; their
-// partial tiles go to a workspace and a second kernel adds them in a fixed
-// order.  Tiles are renumbered so each XCD (8 per chip, each with its own L2)
+// cannot fill the GPU (any of the kernels), K is split over several
+// workgroups per tile; their partial tiles go to a workspace and a second
+// kernel adds them in a fixed order.  Tiles are renumbered so each XCD (8 per chip, each with its own L2)
 // works on a contiguous range of tiles that share rows of X.
 //
 // A simple kernel (128 x 128 tiles, one block per stage) covers K % 64 == 32.

@@ -56,7 +56,8 @@ def weight_bytes(n: int, k: int) -> int:
 
 
 # Sources that define each workload family's kernels: a stored counter
-# figure stays valid while these files are unchanged.
+# figure stays valid while their code (comments and blank space aside) is
+# unchanged.
 KERNEL_SOURCES = {
     "matvec": ("q4_matvec.hip", "q4_device.h"),
     "lmhead": ("q4_matvec.hip", "q4_device.h"),
@@ -65,13 +66,21 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with runs of blank space collapsed
+    (string literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(workload: str) -> str:
-    """Hash of the HIP sources of the workload's kernels."""
+    """Hash of the code of the HIP sources of the workload's kernels."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[workload.split("_")[0]]:
-        with open(os.path.join(ROOT, "q4_quantized_speech_amd", "csrc", name), "rb") as fh:
+        with open(os.path.join(ROOT, "q4_quantized_speech_amd", "csrc", name), encoding="utf-8") as fh:
             h.update(name.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -234,7 +243,7 @@ def _traffic(workload: str, fetch: str, write: str, out: str) -> None:
                  "#   (same with --pmc WRITE_SIZE into <Wr>)\n"
                  "#   python -m q4_quantized_speech_amd.profile_driver traffic W \\\n"
                  "#     --fetch <F>/run_counter_collection.csv --write <Wr>/run_counter_collection.csv\n"
-                 "# W.source_hash ties W's figures to the sources of its kernels.\n")
+                 "# W.source_hash ties W's figures to the code of its kernels' sources (comments aside).\n")
         for k in order:
             fh.write(f"{k}: {vals[k]}\n")
     print(f"{workload}: read {read_b / 1e6:.3f} MB (raw {f_kib:.0f} KiB x {f_fac:.3f}), "

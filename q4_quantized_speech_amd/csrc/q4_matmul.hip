@@ -370,14 +370,16 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 
 // ---------------------------------------------------------------------------
 // Wave-specialised kernel: BM x 256 tiles (BM = 128 or 64), 512 threads,
-// K % 64 == 0.  Waves 0-3 only multiply, each a BM x 64 slice (BM/16 x 4
-// MFMA tiles), reading both operands from LDS in operand order.  Waves 4-7
-// load a stage D stages ahead (each thread one weight row's 36-byte block
-// pair and 16-byte chunks of X), convert X to binary16 and decode the row's
-// two blocks into binary16 (q - 8) d, once per weight.  One barrier per
-// stage.  Measured on the encoder shapes: decoding in the loading waves and
-// D = 2 ran 2-8 % faster than decoding in the multiplying waves from raw
-// codes in LDS with D = 4 (deeper pipelines were slower still).
+// K % 64 == 0.  Waves 0-3 multiply, each a BM x 64 slice (BM/16 x 4 MFMA
+// tiles).  Waves 4-7 load a stage D stages ahead (each thread one weight
+// row's 36-byte block pair and 16-byte chunks of X), convert X to binary16
+// and decode the row's first block into binary16 (q - 8) d in operand order;
+// the second block's codes and scale go to LDS raw (4 dwords per row: the
+// 64 lanes of a fragment read hit 64 distinct banks) and the multiplying
+// waves decode them right before use.  Each weight is decoded once.  One
+// barrier per stage.  Measured on the encoder shapes: splitting the decode
+// this way ran 1-4 % faster than either side decoding both blocks, and D = 2
+// faster than deeper rings.
 // ---------------------------------------------------------------------------
 constexpr int WS_BN = 256, WS_D = 2;
 constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
@@ -393,7 +395,9 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   constexpr int MI = BM / 16;                 // 16-row tiles of X
   constexpr int XU = BM * 16 / WS_PT;         // 16-byte X chunks per producer thread
   __shared__ f16x8 As[2][2][MI][64];          // [buf][block][16-row tile][element]
-  __shared__ f16x8 Bs[2][2][WS_BN / 16][64];  // [buf][block][16-row fragment][lane]: weights
+  __shared__ f16x8 Bs[2][WS_BN / 16][64];     // [buf][16-row fragment][lane]: block 0, binary16
+  __shared__ __attribute__((aligned(16))) uint32_t Wc[2][WS_BN * 4];  // block 1 raw codes, 4 dwords per row
+  __shared__ uint16_t Wsc[2][WS_BN];          // block 1 scales
 
   const int item = xcd_tile(blockIdx.x, gridDim.x);
   const int split = item / ntiles, tile = item % ntiles;
@@ -422,7 +426,14 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       for (int bk = 0; bk < 2; ++bk) {
         f16x8 b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bs[buf][bk][4 * wave + j][lane];
+        for (int j = 0; j < 4; ++j) {
+          if (bk == 0) {
+            b[j] = Bs[buf][4 * wave + j][lane];
+          } else {
+            const int row = 64 * wave + 16 * j + (lane & 15);
+            b[j] = decode8_f16(Wc[buf][row * 4 + ag], Wsc[buf][row]);
+          }
+        }
         const int ae = bk ? ae1 : ae0;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -528,14 +539,14 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
         const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
         *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
       }
-      // the row's two blocks, decoded once into operand order
+      // block 0 decoded here into operand order; block 1 stays raw and is
+      // decoded by the multiplying waves
       const uint32_t* c = rw[slot];
-      f16x8* bw = &Bs[buf][0][tp >> 4][tp & 15];
+      f16x8* bw = &Bs[buf][tp >> 4][tp & 15];
 #pragma unroll
       for (int g = 0; g < 4; ++g) bw[16 * g] = decode8_f16(shift16(c[g + 1], c[g]), c[0] & 0xFFFFu);
-      bw = &Bs[buf][1][tp >> 4][tp & 15];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) bw[16 * g] = decode8_f16(c[5 + g], c[4] >> 16);
+      *reinterpret_cast<u32x4*>(&Wc[buf][tp * 4]) = u32x4{c[5], c[6], c[7], c[8]};
+      Wsc[buf][tp] = static_cast<uint16_t>(c[4] >> 16);
     };
 
     // step t: issue the loads of stage t + D into the register set stage t

@@ -383,7 +383,6 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int WS_BN = 256, WS_D = 2;
 constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
-constexpr int WS_XRS = WS_PT / 16;             // rows per X load round: 16
 constexpr int WS_WU = 9;                       // code dwords per producer thread: one pair
 static_assert(WS_PT == WS_BN, "one weight row per producer thread");
 
@@ -495,16 +494,17 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   } else {
     // ------------------------------- prepare -------------------------------
     const int tp = tid - WS_CONS;  // 0 .. 255
-    // X: chunk xj of rows xr + 16 u (one range-checked resource per 16 rows)
-    const int xj = tp & 15, xr = tp >> 4;
-    __amdgpu_buffer_rsrc_t xrs[XU];
+    // X: one A-operand entry per round -- elements 4g..4g+3 and 16+4g..+3 of
+    // block xb of row xr + 32 u (two 16-byte loads, one 16-byte LDS write;
+    // the 8 lanes of a write cycle hit 8 distinct bank groups)
+    const int xg = tp & 3, xb = (tp >> 2) & 1, xr = tp >> 3;
+    __amdgpu_buffer_rsrc_t xrs[XU / 2];
 #pragma unroll
-    for (int u = 0; u < XU; ++u)
-      xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + WS_XRS * u) * K,
-                         static_cast<int64_t>(M - m0 - WS_XRS * u) * K * 4);
-    const int xvo = xr * K * 4 + xj * 16;
-    const int xb = xj >> 3, xh = (xj >> 2) & 1, xg = xj & 3;
-    const int xe = 16 * xg + (xr ^ (xg + 4 * xb));
+    for (int u = 0; u < XU / 2; ++u)
+      xrs[u] = make_rsrc(X + static_cast<int64_t>(m0 + 32 * u) * K,
+                         static_cast<int64_t>(M - m0 - 32 * u) * K * 4);
+    const int xvo = xr * K * 4 + xb * 128 + xg * 16;
+    const int xe = 16 * xg + ((xr & 15) ^ (xg + 4 * xb));
     // W: this thread's weight row n0 + tp, one 36-byte pair per stage
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + static_cast<int64_t>(n0) * rb,
                                                  static_cast<int64_t>(N - n0) * rb);
@@ -515,9 +515,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     auto load = [&](int t, int slot) {
       const int st = s0 + (t < nst ? t : nst - 1);
 #pragma unroll
-      for (int u = 0; u < XU; ++u)
-        rx[slot][u] = __builtin_bit_cast(
+      for (int u = 0; u < XU / 2; ++u) {
+        rx[slot][2 * u] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo, st * 256, 0));
+        rx[slot][2 * u + 1] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[u], xvo + 64, st * 256, 0));
+      }
       const int wo = wvo + st * PAIR_BYTES;
       const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 0, 0));
       const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, 16, 0));
@@ -532,12 +535,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
     };
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     auto store = [&](int slot, int buf) {
-      char* base = reinterpret_cast<char*>(&As[buf][xb][0][xe]) + 8 * xh;
 #pragma unroll
-      for (int u = 0; u < XU; ++u) {
-        const f32x4 v = rx[slot][u];
-        const u32x2 h = {pk_f16(v.x, v.y), pk_f16(v.z, v.w)};
-        *reinterpret_cast<u32x2*>(base + u * 64 * 16) = h;
+      for (int u = 0; u < XU / 2; ++u) {
+        const f32x4 lo = rx[slot][2 * u], hi = rx[slot][2 * u + 1];
+        const u32x4 h = {pk_f16(lo.x, lo.y), pk_f16(lo.z, lo.w), pk_f16(hi.x, hi.y),
+                         pk_f16(hi.z, hi.w)};
+        *reinterpret_cast<u32x4*>(&As[buf][xb][(xr >> 4) + 2 * u][xe]) = h;
       }
       // block 0 decoded here into operand order; block 1 stays raw and is
       // decoded by the multiplying waves

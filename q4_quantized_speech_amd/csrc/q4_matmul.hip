@@ -426,6 +426,8 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
         f16x8 b[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // first block: decoded by the loading waves; second block: code
+          // dword ag of this lane's weight row, decoded here
           if (bk == 0) {
             b[j] = Bs[buf][4 * wave + j][lane];
           } else {

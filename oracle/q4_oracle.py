@@ -247,9 +247,12 @@ def argmax_accepts(y, bound, idx: int, rel: float = MATVEC_REL,
                    abs_: float = MATVEC_ABS) -> bool:
     """Whether a device argmax ``idx`` is consistent with exact logits ``y``.
 
-    If the top-2 margin exceeds the sum of the two leaders' tolerances the
-    index must be the oracle's; otherwise any row whose exact logit lies within
-    tol_best + tol_idx of the maximum is an acceptable answer.
+    The leaders are the oracle's argmax (lowest index of the maximum) and the
+    runner-up (lowest index of the largest logit among the other rows).  If
+    the margin between them exceeds the sum of those two rows' tolerances, the
+    index must be the oracle's, whatever the tolerances of the other rows.
+    Otherwise the race is too close to call and any row whose exact logit lies
+    within tol_best + tol_idx of the maximum is accepted.
     """
     y = np.asarray(y, dtype=np.float64)
     tol = tolerance(bound, rel, abs_)
@@ -258,6 +261,12 @@ def argmax_accepts(y, bound, idx: int, rel: float = MATVEC_REL,
         return False
     if idx == best:
         return True
+    if y.size > 1:
+        rest = y.copy()
+        rest[best] = -np.inf
+        second = argmax_lowest(rest)
+        if y[best] - y[second] > tol[best] + tol[second]:
+            return False
     return bool(y[idx] >= y[best] - (tol[best] + tol[idx]))
 
 

@@ -372,6 +372,52 @@ def check_argmax(o, seed=19):
     yy = np.array([0.0, 1.0, 1.0 - 1e-5])
     bb = np.array([1.0, 1.0, 1.0])
     assert o.argmax_accepts(yy, bb, 2) and not o.argmax_accepts(yy, bb, 0)
+    check_argmax_clear_margin(o)
+
+
+def check_argmax_clear_margin(o):
+    """The clear-margin clause with unequal bounds: once the top-2 margin
+    exceeds the two leaders' tolerances only the oracle's index is accepted,
+    even where a third row's own tolerance is wide enough to reach the
+    maximum; with a close race that row is accepted.  The absolute term of
+    the bound (1e-6) decides races between rows whose sums of |w x| are 0."""
+    rel, abs_ = o.MATVEC_REL, o.MATVEC_ABS
+    # leaders 1.0 and 0.9 with zero bounds: margin 0.1 >> 2e-6; row 2 lies
+    # 0.15 below the maximum but its bound 2000 gives it a tolerance of 0.2
+    yy = np.array([1.0, 0.9, 0.85])
+    bb = np.array([0.0, 0.0, 2000.0])
+    assert o.argmax_accepts(yy, bb, 0)
+    assert not o.argmax_accepts(yy, bb, 1)
+    assert not o.argmax_accepts(yy, bb, 2)
+    # the same third row in a close race (runner-up 1e-6 below) is accepted
+    yy = np.array([1.0, 1.0 - 1e-6, 0.85])
+    assert o.argmax_accepts(yy, bb, 1) and o.argmax_accepts(yy, bb, 2)
+    # the runner-up is the largest other logit, not the next index, and its
+    # own bound counts: a margin of 0.05 against tolerances 0 + 0.1 is close
+    yy = np.array([0.2, 1.0, 0.3, 0.95])
+    bb = np.array([0.0, 0.0, 0.0, 1000.0])
+    assert o.argmax_accepts(yy, bb, 3)
+    assert not o.argmax_accepts(yy, bb, 2)       # 0.7 below, tolerance 1e-6
+    bb = np.array([1000.0, 0.0, 0.0, 0.0])       # the wide bound on a non-leader
+    assert not o.argmax_accepts(yy, bb, 3)
+    assert not o.argmax_accepts(yy, bb, 0)
+    # rows whose sums of |w x| are 0 (all-zero weights): only the absolute
+    # term separates them, so a gap of 1e-7 < 2e-6 is a close race
+    yy = np.array([1e-7, 0.0])
+    bb = np.array([0.0, 0.0])
+    assert o.argmax_accepts(yy, bb, 0) and o.argmax_accepts(yy, bb, 1)
+    # and a gap of 3e-6 > 2e-6 is not
+    yy = np.array([3e-6, 0.0])
+    assert not o.argmax_accepts(yy, bb, 1)
+    # the relative term: logits 1 and 1 - 1.5e-4 with bounds 1 each give
+    # tolerances 1.01e-4, a close race; with bounds 0.5 (5.1e-5) a clear one
+    yy = np.array([1.0, 1.0 - 1.5e-4])
+    assert o.argmax_accepts(yy, np.array([1.0, 1.0]), 1)
+    assert not o.argmax_accepts(yy, np.array([0.5, 0.5]), 1)
+    # a single row: only index 0
+    assert o.argmax_accepts(np.array([5.0]), np.array([1.0]), 0)
+    assert not o.argmax_accepts(np.array([5.0]), np.array([1.0]), 1)
+    assert abs(rel - 1e-4) == 0 and abs(abs_ - 1e-6) == 0
 
 
 ALL_CHECKS = [

@@ -67,6 +67,18 @@ MUTANTS = [
     ("lmhead panel offset",
      "y[s:e] = w @ xv",
      "y[s:e] = np.roll(w @ xv, 1)"),
+    ("clear margin admits a third row",
+     "if y[best] - y[second] > tol[best] + tol[second]:",
+     "if False:"),
+    ("tolerance without abs",
+     "return rel * np.asarray(bound, dtype=np.float64) + abs_",
+     "return rel * np.asarray(bound, dtype=np.float64)"),
+    ("runner-up is the next index",
+     "second = argmax_lowest(rest)",
+     "second = (best + 1) % y.size"),
+    ("runner-up's bound replaced by the leader's",
+     "if y[best] - y[second] > tol[best] + tol[second]:",
+     "if y[best] - y[second] > 2 * tol[best]:"),
 ]
 
 

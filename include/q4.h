@@ -83,8 +83,10 @@ size_t q4_row_bytes(int64_t K);
  *   1 <= M <= 8, N >= 1, K a positive multiple of 32, N*K < 2^40.
  * Float32 products of the exactly decoded, centred codes (q - 8) with x,
  * float32 accumulation, the block scale applied per block: the error stays
- * within 1e-4 * sum_k |w_k x_k| + 1e-6 for any finite x (a zero weight adds
- * exactly nothing).  Tuned for M = 1; each row of x runs its own workgroups,
+ * within 1e-4 * sum_k |w_k x_k| + 1e-6 for any finite x whose per-block sums
+ * sum_j |q_j - 8| |x_j| stay below the float32 maximum (|x| < 1.3e36
+ * always does; a zero weight, q = 8, adds exactly nothing whatever its x),
+ * and results that fit in float32.  Tuned for M = 1; each row of x runs its own workgroups,
  * which re-read W (mostly from the caches when W is small).  Results are
  * deterministic (fixed reduction order) and a row's result does not depend
  * on the other rows of x.
@@ -109,13 +111,19 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  *             that share a workspace must be ordered.
  * M >= 5: weights and activations are rounded to binary16 (round to nearest
  * even) and multiplied on the matrix cores with float32 accumulation, so |x|
- * must stay below 65504.  M <= 4 (several decode streams) meets the q4_matvec
- * bound for any finite x: either each row of x goes through the q4_matvec
+ * must stay below 65504, and so must every decoded weight: a block whose
+ * scale exceeds 8188 in magnitude (largest |w| above 65504, which an encoder
+ * only writes for weights that large) decodes to +-inf on this path.  M <= 4
+ * (several decode streams) meets the q4_matvec bound, over q4_matvec's range
+ * of x: either each row of x goes through the q4_matvec
  * kernel (one row, K % 64 == 32, and weights small enough that the rows'
  * repeated reads stay in the caches: (M - 1) * N * K * 18/32 bytes up to
  * 40 MiB, K <= 12288), or the weights are read once and enter the matrix
  * cores exactly (q - 8, block scale applied in float32) with x as two
- * binary16 parts after a per-chunk power-of-two scaling.  Deterministic for
+ * binary16 parts after a power-of-two scaling per 256-value chunk of a row;
+ * a chunk whose nonzero magnitudes span more than 2^20 (or reach 2^124) is
+ * summed in float32 instead, so no value of x loses its precision to the
+ * scaling of a larger one.  Deterministic for
  * a given shape, device and ws_bytes; the split changes the order of the
  * float32 sums, so results for different workspace sizes may differ by
  * rounding.
@@ -163,6 +171,25 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x,
                            int32_t* out_idx, float* out_val,
                            int64_t M, int64_t N, int64_t K,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostics: which kernel a call takes (the tests use these to cover every
+ * kernel; a caller may log them).  Both return a static string, or NULL for
+ * a shape the entry point rejects; they enqueue nothing.
+ * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
+ *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel per
+ *   row of x), "small" (M <= 4, weights read once), "skinny" (prompt
+ *   prefixes), "wide128" / "wide64" (tiles of 128 or 64 rows of X by 256
+ *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
+ *   -- and, if splits is not NULL, its number of K splits (1: none).
+ * q4_matvec_route: the kernel variant q4_matvec (argmax == 0) or
+ *   q4_lmhead_argmax (argmax != 0) runs for an N x K matrix -- "pairs_lds_g4"
+ *   (x in LDS, four row groups per workgroup: 65536 rows or more),
+ *   "pairs_lds" (x in LDS), "pairs_reg_r1" / "pairs_reg_r2" (x in registers,
+ *   one or two rows per lane and pass) or "any" (K % 64 == 32, or K > 12288).
+ */
+const char* q4_matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int32_t* splits);
+const char* q4_matvec_route(int64_t N, int64_t K, int32_t argmax);
 
 /*
  * q4_quantize -- device-side GGUF Q4_0 encoder, used to prepare weights:

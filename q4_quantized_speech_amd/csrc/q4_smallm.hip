@@ -13,6 +13,15 @@
 //    scaling each row's 256-value chunk by the power of two that puts its
 //    largest magnitude in [2^14, 2^15) (range safe, undone exactly after the
 //    chunk): two MFMAs per block carry about 22 significant bits of x;
+//  * that holds for the values of a chunk within 2^20 of its largest: they
+//    scale to at least 2^-6, where the two parts keep a relative error below
+//    2^-19.  A chunk (of one row of x) whose nonzero magnitudes span more
+//    than 2^20, or whose largest is 2^124 or more (or not finite), would lose
+//    its small values to binary16 subnormals or overflow; it is "wide": its
+//    binary16 operands are zero, and the waves add its products with float32
+//    FMAs of the centred codes (q - 8) against the float32 x, as q4_matvec
+//    does.  Normal activations rarely have one (a value below 2^-20 of the
+//    chunk's largest), so the float32 path costs nothing in practice;
 //  * a workgroup owns 64 rows of W (four waves of 16 rows) and a range of K,
 //    taken in segments of four 256-value chunks; x of a segment is staged in
 //    LDS in the MFMA operand layout (wave w stages chunk w), shared by the
@@ -92,6 +101,21 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Smallest of a non-negative value over the wave, in every lane (the same
+// pattern of exchanges as wave_max_nonneg).
+__device__ __forceinline__ float wave_min_nonneg(float v) {
+  v = fminf(v, dpp_f32<0xB1>(v));
+  v = fminf(v, dpp_f32<0x4E>(v));
+  v = fminf(v, dpp_f32<0x124>(v));
+  v = fminf(v, dpp_f32<0x128>(v));
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Power-of-two exponent that scales a row whose largest magnitude has the
 // float bits `mbits` (non-negative) into [2^14, 2^15); clamped so that the
 // scale and its inverse stay normal floats.
@@ -116,6 +140,10 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
   __shared__ f16x8 xh[SM_SEGB][4][MR + 1];
   __shared__ f16x8 xl[SM_SEGB][4][MR + 1];
   __shared__ f32x4m usc[SM_SEGC][4];  // [chunk][row / 4]: 2^-scale of each row of x
+  // wide chunks: the float32 x of each (chunk, row), and per chunk a bit
+  // mask of the rows whose chunk is wide (0: all rows on the matrix cores)
+  __shared__ __attribute__((aligned(16))) float xf[SM_SEGC][MR][256];
+  __shared__ uint32_t wflag[SM_SEGC];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -163,31 +191,52 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
   };
   // Each row's chunk is scaled by the power of two that puts its largest
   // magnitude in [2^14, 2^15) (a wave maximum: one chunk is one wave), split
-  // into hi/lo binary16 and stored in operand order.
+  // into hi/lo binary16 and stored in operand order; a wide chunk (see the
+  // header) stores zero operands and its float32 values instead.
   auto stage_store = [&](const f32x4m (&v)[MR]) {
     const int k = 4 * lane, blk = wave * 8 + (k >> 5), e = k & 31;
     const int gg = (e & 15) >> 2, half = e >> 4;  // operand group, low/high nibble half
+    uint32_t wmask = 0;
 #pragma unroll
     for (int u = 0; u < MR; ++u) {
       if (u < M) {
-        const float a = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
-        const int se = scale_exp(__float_as_uint(wave_max_nonneg(a)));
-        const f32x4m xv = v[u] * exp2i(se);
-        const f16x2 h01 = {static_cast<_Float16>(xv.x), static_cast<_Float16>(xv.y)};
-        const f16x2 h23 = {static_cast<_Float16>(xv.z), static_cast<_Float16>(xv.w)};
-        const f16x2 l01 = {static_cast<_Float16>(xv.x - static_cast<float>(h01[0])),
-                           static_cast<_Float16>(xv.y - static_cast<float>(h01[1]))};
-        const f16x2 l23 = {static_cast<_Float16>(xv.z - static_cast<float>(h23[0])),
-                           static_cast<_Float16>(xv.w - static_cast<float>(h23[1]))};
+        const f32x4m av = {fabsf(v[u].x), fabsf(v[u].y), fabsf(v[u].z), fabsf(v[u].w)};
+        const float a = fmaxf(fmaxf(av.x, av.y), fmaxf(av.z, av.w));
+        // smallest nonzero magnitude (+inf when all four are zero; NaN never
+        // counts, in neither reduction)
+        float z = __builtin_inff();
+        z = av.x > 0.f ? fminf(z, av.x) : z;
+        z = av.y > 0.f ? fminf(z, av.y) : z;
+        z = av.z > 0.f ? fminf(z, av.z) : z;
+        z = av.w > 0.f ? fminf(z, av.w) : z;
+        const float cmax = wave_max_nonneg(a);
+        const float cmin = wave_min_nonneg(z);
+        // the same in every lane of the wave (both reductions end in all lanes)
+        const bool wide = !(cmax < 0x1p124f) || cmin < cmax * 0x1p-20f;
+        const int se = scale_exp(__float_as_uint(cmax));
         uint32_t* ph = reinterpret_cast<uint32_t*>(&xh[blk][gg][u]) + 2 * half;
         uint32_t* pl = reinterpret_cast<uint32_t*>(&xl[blk][gg][u]) + 2 * half;
-        ph[0] = __builtin_bit_cast(uint32_t, h01);
-        ph[1] = __builtin_bit_cast(uint32_t, h23);
-        pl[0] = __builtin_bit_cast(uint32_t, l01);
-        pl[1] = __builtin_bit_cast(uint32_t, l23);
+        if (wide) {
+          ph[0] = ph[1] = pl[0] = pl[1] = 0u;
+          *reinterpret_cast<f32x4m*>(&xf[wave][u][k]) = v[u];
+          wmask |= 1u << u;
+        } else {
+          const f32x4m xv = v[u] * exp2i(se);
+          const f16x2 h01 = {static_cast<_Float16>(xv.x), static_cast<_Float16>(xv.y)};
+          const f16x2 h23 = {static_cast<_Float16>(xv.z), static_cast<_Float16>(xv.w)};
+          const f16x2 l01 = {static_cast<_Float16>(xv.x - static_cast<float>(h01[0])),
+                             static_cast<_Float16>(xv.y - static_cast<float>(h01[1]))};
+          const f16x2 l23 = {static_cast<_Float16>(xv.z - static_cast<float>(h23[0])),
+                             static_cast<_Float16>(xv.w - static_cast<float>(h23[1]))};
+          ph[0] = __builtin_bit_cast(uint32_t, h01);
+          ph[1] = __builtin_bit_cast(uint32_t, h23);
+          pl[0] = __builtin_bit_cast(uint32_t, l01);
+          pl[1] = __builtin_bit_cast(uint32_t, l23);
+        }
         if (lane == 0) usc[wave][u >> 2][u & 3] = exp2i(-se);
       }
     }
+    if (lane == 0) wflag[wave] = wmask;
   };
 
   // One chunk (4 pairs = 8 blocks) of this wave's 16 rows; cs = chunk index
@@ -225,6 +274,36 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
     acc.y = __builtin_fmaf(cacc.y, u.y, acc.y);
     acc.z = __builtin_fmaf(cacc.z, u.z, acc.z);
     acc.w = __builtin_fmaf(cacc.w, u.w, acc.w);
+    // Wide chunks (rare; the mask is the same for the whole workgroup): the
+    // lane's 8 weights of each block against the float32 x, centred codes,
+    // the block scale per block; the four lane groups' sums are added in a
+    // fixed order and land in every lane.  Lane group 0 holds rows 0..3 of
+    // x in acc's components; the other groups' components are rows past 4,
+    // never stored, so the sum is added in every lane without a branch.
+    const uint32_t wm = wflag[cs];
+    if (wm != 0u) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        if ((wm >> r) & 1u) {
+          const float* xr = &xf[cs][r][0];
+          float part = 0.f;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int b32 = 32 * (2 * p + h);
+              const f32x4m xlo = *reinterpret_cast<const f32x4m*>(xr + b32 + 4 * g);
+              const f32x4m xhi = *reinterpret_cast<const f32x4m*>(xr + b32 + 16 + 4 * g);
+              const float d = half_bits_to_float(h ? (S[p] >> 16) : (S[p] & 0xFFFFu));
+              part = __builtin_fmaf(d, nib_dot4_centred(h ? O[p] : E[p], xlo, xhi, 0.f), part);
+            }
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          acc[r] += part;
+        }
+      }
+    }
   };
 
   {  // operand entries of rows >= M (and the zero entry) stay zero throughout

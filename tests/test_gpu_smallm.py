@@ -53,16 +53,23 @@ def test_small_m_matvec_bound(m, n, k):
 
 
 @pytest.mark.parametrize("k", [1280, 12352])
-@pytest.mark.parametrize("case", ["tiny", "huge", "spread", "zero_row", "mixed_rows"])
+@pytest.mark.parametrize("case", ["tiny", "huge", "spread", "zero_row", "mixed_rows",
+                                  "outlier_1e9", "outlier_1e11", "outlier_1e30", "outlier_3e38",
+                                  "huge_3e35", "tiny_among_normal"])
 def test_small_m_x_range(case, k):
     """x far from 1 keeps the bound on both routes (K = 12352: the small-M
     kernel's per-chunk power-of-two scaling): all tiny, all huge (past
     binary16's range), one large value among small ones, a row of zeros, rows
-    of very different magnitudes."""
+    of very different magnitudes; huge values on zero-weight columns (they
+    set a chunk's scale but add nothing, so the chunk's other values must
+    keep their precision: the kernel's float32 path for wide chunks); chunks
+    of +-1e38 against a few nonzero weight columns (scaling them for binary16
+    would overflow); tiny values scattered among normal ones."""
     m, n = 4, 96
-    qb = _w(n, k, 5)
     g = np.random.Generator(np.random.PCG64(6))
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
     x = g.standard_normal((m, k))
+    cols = [3, 77, k // 2 + 5, k - 1]
     if case == "tiny":
         x *= 1e-30
     elif case == "huge":
@@ -72,8 +79,18 @@ def test_small_m_x_range(case, k):
         x[:, 77] = 1e4
     elif case == "zero_row":
         x[2] = 0.0
-    else:
+    elif case == "mixed_rows":
         x *= np.array([1e-20, 1e8, 1e-3, 1e-12])[:, None]
+    elif case.startswith("outlier"):
+        w[:, cols] = 0.0                       # a zero column quantises to code 8
+        x[:, cols] = float(case.split("_")[1])
+        x[1, cols] *= -1.0
+    elif case == "huge_3e35":
+        x *= 3e35
+        x[2] *= 1e-10                          # one row far below the others
+    else:
+        x[:, ::97] *= 1e-9
+    qb = O.quantize_q4_0(w)
     x = x.astype(np.float32)
     ref, b = O.matmul_f64(qb, x, n, k)
     announce(f"small-M x range {case} k={k}")

@@ -61,6 +61,8 @@ _SIGS = {
     "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_quantize": ([_P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "q4_matmul_route": ([_I64, _I64, _I64, _SZ, _P], ctypes.c_char_p),
+    "q4_matvec_route": ([_I64, _I64, ctypes.c_int32], ctypes.c_char_p),
     "q4_gguf_open": ([_P, _I64, _P], ctypes.c_int),
     "q4_gguf_close": ([_P], None),
     "q4_gguf_version": ([_P], ctypes.c_uint32),
@@ -111,6 +113,17 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context in which tensors this module allocates (outputs, workspaces,
+    flags) come from ``stream``'s pool and their fills run on ``stream``: the
+    library's kernel runs there, so nothing else orders them before it, and
+    a buffer freed back to another stream's pool could be reused by that
+    stream while the kernel still writes it.  The caller orders its own
+    inputs with ``stream``."""
+    import contextlib
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -151,10 +164,12 @@ def matvec(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     squeeze = x.dim() == 1
     x2 = _as_2d_f32(x, k)
     m = x2.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _need_cuda(w_q4, x2, out)
-    _check(lib().q4_matvec(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _stream(stream)), "q4_matvec")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        _need_cuda(w_q4, x2, out)
+        _check(lib().q4_matvec(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _stream(stream)),
+               "q4_matvec")
     return out.view(n) if squeeze else out
 
 
@@ -177,17 +192,35 @@ def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     n, k = q4_shape(w_q4)
     x2 = _as_2d_f32(x, k)
     m = x2.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    if workspace is True:
-        workspace = matmul_workspace(m, n, k, x.device)
-    elif workspace is False:
-        workspace = None
-    _need_cuda(w_q4, x2, out, workspace)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _ptr(workspace), ws_bytes,
-                           _stream(stream)), "q4_matmul")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        if workspace is True:
+            workspace = matmul_workspace(m, n, k, x.device)
+        elif workspace is False:
+            workspace = None
+        _need_cuda(w_q4, x2, out, workspace)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _ptr(workspace), ws_bytes,
+                               _stream(stream)), "q4_matmul")
     return out
+
+
+def matmul_route(m: int, n: int, k: int, ws_bytes: int = 0):
+    """(kernel name, K splits) q4_matmul takes for the shape and workspace size."""
+    sp = ctypes.c_int32(0)
+    r = lib().q4_matmul_route(m, n, k, ws_bytes, ctypes.byref(sp))
+    if r is None:
+        raise ValueError(f"q4_matmul rejects M={m} N={n} K={k}")
+    return r.decode(), int(sp.value)
+
+
+def matvec_route(n: int, k: int, argmax: bool = False) -> str:
+    """Kernel variant q4_matvec (or q4_lmhead_argmax) takes for an N x K matrix."""
+    r = lib().q4_matvec_route(n, k, 1 if argmax else 0)
+    if r is None:
+        raise ValueError(f"rejected shape N={n} K={k}")
+    return r.decode()
 
 
 def embed_rows(table_q4: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None,
@@ -197,11 +230,12 @@ def embed_rows(table_q4: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | No
     if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
         raise ValueError("ids must be a contiguous int32 vector")
     m = ids.shape[0]
-    if out is None:
-        out = torch.empty((m, k), dtype=torch.float32, device=ids.device)
-    _need_cuda(table_q4, ids, out)
-    _check(lib().q4_embed_rows(_ptr(table_q4), _ptr(ids), _ptr(out), m, n, k, _stream(stream)),
-           "q4_embed_rows")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((m, k), dtype=torch.float32, device=ids.device)
+        _need_cuda(table_q4, ids, out)
+        _check(lib().q4_embed_rows(_ptr(table_q4), _ptr(ids), _ptr(out), m, n, k, _stream(stream)),
+               "q4_embed_rows")
     return out
 
 
@@ -221,16 +255,17 @@ def lmhead_argmax(w_q4: torch.Tensor, x: torch.Tensor, workspace: torch.Tensor |
     n, k = q4_shape(w_q4)
     x2 = _as_2d_f32(x, k)
     m = x2.shape[0]
-    if workspace is None:
-        workspace = lmhead_workspace(m, x.device)
-    if out_idx is None:
-        out_idx = torch.empty(m, dtype=torch.int32, device=x.device)
-    if out_val is None:
-        out_val = torch.empty(m, dtype=torch.float32, device=x.device)
-    _need_cuda(w_q4, x2, workspace, out_idx, out_val)
-    _check(lib().q4_lmhead_argmax(_ptr(w_q4), _ptr(x2), _ptr(out_idx), _ptr(out_val), m, n, k,
-                                  _ptr(workspace), workspace.numel(), _stream(stream)),
-           "q4_lmhead_argmax")
+    with _on(stream):
+        if workspace is None:
+            workspace = lmhead_workspace(m, x.device)   # zero-filled on `stream`
+        if out_idx is None:
+            out_idx = torch.empty(m, dtype=torch.int32, device=x.device)
+        if out_val is None:
+            out_val = torch.empty(m, dtype=torch.float32, device=x.device)
+        _need_cuda(w_q4, x2, workspace, out_idx, out_val)
+        _check(lib().q4_lmhead_argmax(_ptr(w_q4), _ptr(x2), _ptr(out_idx), _ptr(out_val), m, n, k,
+                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+               "q4_lmhead_argmax")
     return out_idx, out_val
 
 
@@ -241,12 +276,16 @@ def quantize(w: torch.Tensor, out: torch.Tensor | None = None, check: bool = Tru
     n, k = w.shape
     if k % QK:
         raise ValueError("K must be a multiple of 32")
-    if out is None:
-        out = torch.empty((n, k // QK * BLOCK_BYTES), dtype=torch.uint8, device=w.device)
-    flag = torch.zeros(4, dtype=torch.int32, device=w.device) if check else None
-    _need_cuda(w, out, flag)
-    _check(lib().q4_quantize(_ptr(w), _ptr(out), n, k, _ptr(flag), _stream(stream)), "q4_quantize")
-    if check and int(flag[0].item()) != 0:
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n, k // QK * BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+        flag = torch.zeros(4, dtype=torch.int32, device=w.device) if check else None
+        _need_cuda(w, out, flag)
+        _check(lib().q4_quantize(_ptr(w), _ptr(out), n, k, _ptr(flag), _stream(stream)),
+               "q4_quantize")
+        # the copy behind item() runs on `stream`, after the kernel
+        bad = check and int(flag[0].item()) != 0
+    if bad:
         raise ValueError("q4_quantize: non-finite input or a scale overflowing binary16")
     return out
 

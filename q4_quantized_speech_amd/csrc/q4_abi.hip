@@ -131,10 +131,25 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x, int32_t* out_idx, f
                                          N, K, workspace, static_cast<hipStream_t>(stream)));
 }
 
+const char* q4_matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int32_t* splits) {
+  if (!matmul_shape_ok(M, N, K)) return nullptr;
+  int sp = 1;
+  const char* r = matmul_route(M, N, K, ws_bytes, device_info().cu_count, &sp);
+  if (splits) *splits = sp;
+  return r;
+}
+
+const char* q4_matvec_route(int64_t N, int64_t K, int32_t argmax) {
+  if (N < 1 || N >= (int64_t(1) << 31) || !k_ok(K) || N * K >= (int64_t(1) << 40)) return nullptr;
+  return matvec_route(N, K, argmax != 0);
+}
+
 q4_status q4_quantize(const float* w, void* w_q4, int64_t N, int64_t K, int32_t* flag,
                       void* stream) {
   if (!w || !w_q4) return Q4_ERR_NULL;
-  if (N < 1 || !k_ok(K) || N * (K / 32) >= (int64_t(1) << 37)) return Q4_ERR_SHAPE;
+  // N is bounded before the product (K / 32 <= 2^25), so nothing overflows
+  if (N < 1 || N >= (int64_t(1) << 37) || !k_ok(K) || N * (K / 32) >= (int64_t(1) << 37))
+    return Q4_ERR_SHAPE;
   if (!aligned16(w) || !aligned16(w_q4) || (flag && (reinterpret_cast<uintptr_t>(flag) & 3u)))
     return Q4_ERR_ALIGN;
   return hip_status(launch_quantize(w, static_cast<uint8_t*>(w_q4), N, K, flag,

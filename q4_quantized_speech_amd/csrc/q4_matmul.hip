@@ -1010,6 +1010,21 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
   return MatmulPlan{kind, (nstg + per - 1) / per, per};  // every split non-empty
 }
 
+const char* matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int cus, int* splits) {
+  const MatmulPlan p = plan_matmul(M, N, K, cus, ws_bytes);
+  if (splits) *splits = p.splits;
+  switch (p.kind) {
+    case MM_STREAM: return "matvec";
+    case MM_SMALL: return "small";
+    case MM_SKINNY: return "skinny";
+    case MM_WIDE: return "wide128";
+    case MM_WIDE64: return "wide64";
+    case MM_TILE: return "tile";
+    case MM_SIMPLE: return "simple";
+  }
+  return "unknown";
+}
+
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
   const MatmulPlan p = plan_matmul(M, N, K, cus, SIZE_MAX);
   return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;

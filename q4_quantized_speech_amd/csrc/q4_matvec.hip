@@ -136,9 +136,13 @@ __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
 // calls.  key = order-preserving bits of the value (high word) | ~index (low
 // word), so the largest key is the largest value with the lowest index, and
 // 0 means "no candidate" (NaN never enters).  Each workgroup folds its
-// candidate in with one device-scope atomic max, waits for it to complete,
-// then counts itself in; the workgroup that arrives last reads the key,
-// writes the outputs and clears both words for the next call.
+// candidate in with one device-scope atomic max, then counts itself in with
+// a release increment (its max is ordered before its count); the workgroup
+// that arrives last takes an acquire fence, which makes every earlier
+// release (every other workgroup's max) visible to it, reads the key, writes
+// the outputs and clears both words for the next call.  Only that workgroup
+// pays for the acquire (an invalidation of its L2): in every workgroup it
+// cost ~7 us on the 131072-row table.
 constexpr int AM_ROW_BYTES = 256;
 __device__ __forceinline__ uint64_t am_key(float v, int i) {
   if (i < 0 || v != v) return 0;
@@ -155,10 +159,10 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
   am_block_reduce(bv, bi);
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_max(key, am_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // the max is performed before the count moves
     const uint32_t prev =
-        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == static_cast<uint32_t>(nwg - 1)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const uint64_t k = __hip_atomic_load(key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(key, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -451,44 +455,68 @@ PairGrid pair_grid(int64_t N) {
 // start-up; one row per lane halves the pass granularity and is used only
 // where two would leave CUs idle and one gives the busiest CU fewer rows.
 constexpr int64_t MV_GROUPED_ROWS = 65536;
+enum PairVariant { PV_LDS_G4, PV_LDS, PV_REG_R1, PV_REG_R2 };
+template <int KS, bool ARGMAX>
+PairVariant pair_variant(int64_t N) {
+  if (KS <= 4 && N >= MV_GROUPED_ROWS) return PV_LDS_G4;
+  if (KS <= 4 && !ARGMAX) return PV_LDS;
+  const PairGrid g2 = pair_grid<KS, ARGMAX, 2, false, 1>(N);
+  const PairGrid g1 = pair_grid<KS, ARGMAX, 1, false, 1>(N);
+  const bool one = g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows;
+  return one ? PV_REG_R1 : PV_REG_R2;
+}
+
+template <int KS, bool ARGMAX, int R, bool XL, int G>
+void launch_variant(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
+                    int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const PairGrid g = pair_grid<KS, ARGMAX, R, XL, G>(N);
+  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, R, XL, G>),
+                     dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS * G), 0, s, w, x, y, idx,
+                     val, ws, N, static_cast<int>(K));
+}
+
 template <int KS, bool ARGMAX>
 void launch_pairs(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
-                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if constexpr (KS <= 4) {
-    if (N >= MV_GROUPED_ROWS) {
-      const PairGrid g = pair_grid<KS, ARGMAX, 1, true, 4>(N);
-      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true, 4>),
-                         dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS * 4), 0, s, w, x, y,
-                         idx, val, ws, N, static_cast<int>(K));
-      return;
-    }
+                  int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  switch (pair_variant<KS, ARGMAX>(N)) {
+    case PV_LDS_G4:
+      if constexpr (KS <= 4) launch_variant<KS, ARGMAX, 1, true, 4>(w, x, y, idx, val, ws, M, N, K, s);
+      break;
+    case PV_LDS:
+      if constexpr (KS <= 4 && !ARGMAX)
+        launch_variant<KS, ARGMAX, 1, true, 1>(w, x, y, idx, val, ws, M, N, K, s);
+      break;
+    case PV_REG_R1:
+      launch_variant<KS, ARGMAX, 1, false, 1>(w, x, y, idx, val, ws, M, N, K, s);
+      break;
+    case PV_REG_R2:
+      launch_variant<KS, ARGMAX, 2, false, 1>(w, x, y, idx, val, ws, M, N, K, s);
+      break;
   }
-  if constexpr (KS <= 4 && !ARGMAX) {
-    const PairGrid g = pair_grid<KS, ARGMAX, 1, true, 1>(N);
-    hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, true, 1>),
-                       dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS), 0, s, w, x, y, idx, val,
-                       ws, N, static_cast<int>(K));
-  } else {
-    const PairGrid g2 = pair_grid<KS, ARGMAX, 2, false, 1>(N);
-    const PairGrid g1 = pair_grid<KS, ARGMAX, 1, false, 1>(N);
-    const bool one = g2.g < device_info().cu_count && g1.g > g2.g && g1.cu_rows < g2.cu_rows;
-    if (one)
-      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 1, false, 1>),
-                         dim3(static_cast<unsigned>(g1.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
-                         val, ws, N, static_cast<int>(K));
-    else
-      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, 2, false, 1>),
-                         dim3(static_cast<unsigned>(g2.g), M), dim3(64 * KS), 0, s, w, x, y, idx,
-                         val, ws, N, static_cast<int>(K));
+}
+
+// Pair-kernel waves per workgroup for K, or 0 for the generic kernel (K % 64
+// == 32, or rows longer than 12288: more than 12 waves per workgroup would cap
+// registers below the lane's x slice).
+int64_t pair_ks(int64_t K) { return (K % 64 == 0 && K <= 12288) ? (K / 64 + 15) / 16 : 0; }
+
+template <bool ARGMAX>
+const char* route_mv(int64_t N, int64_t K) {
+  static const char* names[] = {"pairs_lds_g4", "pairs_lds", "pairs_reg_r1", "pairs_reg_r2"};
+  switch (pair_ks(K)) {
+#define Q4_MV_CASE(n) \
+  case n: return names[pair_variant<n, ARGMAX>(N)];
+    Q4_MV_CASE(1) Q4_MV_CASE(2) Q4_MV_CASE(3) Q4_MV_CASE(4) Q4_MV_CASE(5) Q4_MV_CASE(6)
+    Q4_MV_CASE(7) Q4_MV_CASE(8) Q4_MV_CASE(9) Q4_MV_CASE(10) Q4_MV_CASE(11) Q4_MV_CASE(12)
+#undef Q4_MV_CASE
+    default: return "any";
   }
 }
 
 template <bool ARGMAX>
 hipError_t launch_mv(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val,
                      void* ws, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  // more than 12 waves per workgroup would cap registers below the lane's x slice
-  const int64_t ks = (K % 64 == 0 && K <= 12288) ? (K / 64 + 15) / 16 : 0;
-  switch (ks) {
+  switch (pair_ks(K)) {
 #define Q4_MV_CASE(n) \
   case n: launch_pairs<n, ARGMAX>(w, x, y, idx, val, ws, M, N, K, s); break;
     Q4_MV_CASE(1) Q4_MV_CASE(2) Q4_MV_CASE(3) Q4_MV_CASE(4) Q4_MV_CASE(5) Q4_MV_CASE(6)
@@ -511,6 +539,10 @@ hipError_t launch_mv(const uint8_t* w, const float* x, float* y, int32_t* idx, f
 hipError_t launch_matvec(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, hipStream_t s) {
   return launch_mv<false>(w, x, y, nullptr, nullptr, nullptr, M, N, K, s);
+}
+
+const char* matvec_route(int64_t N, int64_t K, bool argmax) {
+  return argmax ? route_mv<true>(N, K) : route_mv<false>(N, K);
 }
 
 size_t lmhead_workspace_bytes(int64_t M) {

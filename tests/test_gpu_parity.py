@@ -206,9 +206,14 @@ def test_matvec_single_3072():
 def test_matmul_one_hot_f16():
     n, k = 150, 256
     w = _rand_w(n, k, 77)
-    # make one row carry example D's 0.0624847... code so the tie-to-even shows
     qb = O.quantize_q4_0(w)
+    # block 2 of row 3 becomes golden block D, whose decoded 0.0624847... and
+    # -0.0874786... round to binary16 as the golden file states
+    d = {g["name"]: g for g in oc.load_golden()}["D"]
+    qb[3, 2 * 18: 3 * 18] = np.frombuffer(d["bytes"], np.uint8)
     wd = O.dequantize_q4_0(qb, n, k)
+    for i, v in d["f16"].items():
+        assert O.round_f16(wd[3, 64 + i: 65 + i])[0] == v
     x = np.zeros((k, k), np.float32)
     np.fill_diagonal(x, 1.0)
     announce("matmul one-hot")

@@ -189,39 +189,43 @@ def _bad(tmp_path, blob):
     return _open_status([_write(tmp_path, blob, "bad.gguf")])
 
 
-def test_malformed_headers(tmp_path):
+def malformed_cases():
+    """(name, bytes) of files the reader must refuse with Q4_ERR_FORMAT."""
     blob, start, offs, meta, tensors, _ = _model()
-    F = q4.Q4_ERR_FORMAT
-    assert _bad(tmp_path, b"GGUX" + blob[4:]) == F
-    assert _bad(tmp_path, blob[:4] + struct.pack("<I", 1) + blob[8:]) == F
-    assert _bad(tmp_path, blob[:4] + struct.pack("<I", 4) + blob[8:]) == F
-    assert _bad(tmp_path, b"") == F
+    out = [("magic", b"GGUX" + blob[4:]),
+           ("version 1", blob[:4] + struct.pack("<I", 1) + blob[8:]),
+           ("version 4", blob[:4] + struct.pack("<I", 4) + blob[8:]),
+           ("empty", b"")]
     # every truncation inside the header or the data is refused
     for cut in sorted({3, 4, 8, 23, 24, 30, 100, start - 1, start, start + offs[-2] + 1}):
-        assert _bad(tmp_path, blob[:cut]) == F, cut
+        out.append((f"cut {cut}", blob[:cut]))
     # absurd counts are refused before anything is allocated for them
-    assert _bad(tmp_path, blob[:8] + struct.pack("<QQ", 1 << 62, 1) + blob[24:]) == F
-    assert _bad(tmp_path, blob[:8] + struct.pack("<QQ", 1, 1 << 62) + blob[24:]) == F
-    # misaligned tensor offset
-    assert _bad(tmp_path, W.build(meta, tensors, offsets=[0, 2048, 4096, 6144, 8192, 10001])[0]) == F
-    # duplicate tensor names
+    out.append(("tensor count 2^62", blob[:8] + struct.pack("<QQ", 1 << 62, 1) + blob[24:]))
+    out.append(("metadata count 2^62", blob[:8] + struct.pack("<QQ", 1, 1 << 62) + blob[24:]))
+    out.append(("misaligned offset",
+                W.build(meta, tensors, offsets=[0, 2048, 4096, 6144, 8192, 10001])[0]))
     dup = [tensors[1], ("output_norm.weight",) + tensors[1][1:]]
-    assert _bad(tmp_path, W.build([], dup)[0]) == F
-    # tensor past the end of the data section
-    assert _bad(tmp_path, W.build([], [tensors[1]], offsets=[64])[0][:-8]) == F
+    out.append(("duplicate names", W.build([], dup)[0]))
+    out.append(("tensor past the end", W.build([], [tensors[1]], offsets=[64])[0][:-8]))
     # alignment that is not a power of two, or not an integer
     for a in (0, 24):
-        assert _bad(tmp_path, W.build([("general.alignment", W.U32, a)], [])[0]) == F
-    assert _bad(tmp_path, W.build([("general.alignment", W.F32, 32.0)], [])[0]) == F
+        out.append((f"alignment {a}", W.build([("general.alignment", W.U32, a)], [])[0]))
+    out.append(("float alignment", W.build([("general.alignment", W.F32, 32.0)], [])[0]))
     # rank 0 and rank 5 tensors, a zero dimension
     for dims in [(), (1, 1, 1, 1, 32), (0, 32)]:
-        assert _bad(tmp_path, W.build([], [("x", dims, W.T_F32, b"")])[0]) == F, dims
+        out.append((f"dims {dims}", W.build([], [("x", dims, W.T_F32, b"")])[0]))
     # unknown metadata value type, bool outside {0, 1}, nested array
     raw = W.build([("k", W.U8, 1)], [])[0]
-    assert _bad(tmp_path, raw[:24 + 8 + 1] + struct.pack("<I", 13) + raw[24 + 8 + 1 + 4:]) == F
-    assert _bad(tmp_path, W.build([("k", W.U8, 2)], [])[0].replace(
-        struct.pack("<IB", W.U8, 2), struct.pack("<IB", W.BOOL, 2))) == F
-    assert _bad(tmp_path, W.build([("k", W.ARRAY, (W.ARRAY, []))], [])[0]) == F
+    out.append(("value type 13", raw[:24 + 8 + 1] + struct.pack("<I", 13) + raw[24 + 8 + 1 + 4:]))
+    out.append(("bool 2", W.build([("k", W.U8, 2)], [])[0].replace(
+        struct.pack("<IB", W.U8, 2), struct.pack("<IB", W.BOOL, 2))))
+    out.append(("nested array", W.build([("k", W.ARRAY, (W.ARRAY, []))], [])[0]))
+    return out
+
+
+def test_malformed_headers(tmp_path):
+    for name, blob in malformed_cases():
+        assert _bad(tmp_path, blob) == q4.Q4_ERR_FORMAT, name
 
 
 def test_empty_and_unpadded_files(tmp_path):

@@ -136,13 +136,23 @@ __device__ __forceinline__ void am_block_reduce(float& bv, int& bi) {
 // calls.  key = order-preserving bits of the value (high word) | ~index (low
 // word), so the largest key is the largest value with the lowest index, and
 // 0 means "no candidate" (NaN never enters).  Each workgroup folds its
-// candidate in with one device-scope atomic max, then counts itself in with
-// a release increment (its max is ordered before its count); the workgroup
-// that arrives last takes an acquire fence, which makes every earlier
-// release (every other workgroup's max) visible to it, reads the key, writes
-// the outputs and clears both words for the next call.  Only that workgroup
-// pays for the acquire (an invalidation of its L2): in every workgroup it
-// cost ~7 us on the 131072-row table.
+// candidate in with one device-scope atomic max, then counts itself in; the
+// workgroup that arrives last takes an acquire fence, reads the key, writes
+// the outputs and clears both words for the next call.
+// Ordering, in the memory model's terms: a workgroup whose max raised the
+// key (the max returns the old key) counts itself in with a release
+// increment, which orders its max before its count; one whose max changed
+// nothing has nothing to publish and counts itself in relaxed.  The
+// increments all act on one counter, so every release heads a release
+// sequence that the later increments continue, and the last workgroup's
+// increment reads the end of it: its acquire fence synchronizes with every
+// raising workgroup's release, and its read of the key sees at least every
+// raised value -- the largest key among them is the largest of all (a
+// workgroup whose max changed nothing saw a key at least as large, written
+// by a raising one).  A release is an L2 writeback and an acquire an L2
+// invalidation on this chip, each costing ~6 us on the 131072-row table when
+// every workgroup took them; in arrival order only a few workgroups (about
+// the logarithm of their number) raise the key.
 constexpr int AM_ROW_BYTES = 256;
 __device__ __forceinline__ uint64_t am_key(float v, int i) {
   if (i < 0 || v != v) return 0;
@@ -158,9 +168,13 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
   uint32_t* count = reinterpret_cast<uint32_t*>(row + 128);
   am_block_reduce(bv, bi);
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_max(key, am_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev =
-        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t mine = am_key(bv, bi);
+    const uint64_t old = __hip_atomic_fetch_max(key, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t prev;
+    if (mine > old)
+      prev = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      prev = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == static_cast<uint32_t>(nwg - 1)) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const uint64_t k = __hip_atomic_load(key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

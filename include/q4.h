@@ -173,6 +173,20 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * q4_lmhead_argmax_noalloc -- q4_lmhead_argmax for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * q4_lmhead_argmax without the workspace: its place is taken by a fixed
+ * 16 KiB array in the library's own device memory (one per GPU, held until
+ * the process ends), so 1 <= M <= 64 (Q4_ERR_SHAPE beyond).  Allocates
+ * nothing.  The first call on a device also enqueues one small kernel that
+ * clears that array.  Every call on one GPU shares the array, so calls that
+ * may overlap on one GPU (unordered streams) race: the caller orders them.
+ */
+q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* out_idx,
+                                   float* out_val, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Diagnostics: which kernel a call takes (the tests use these to cover every
  * kernel; a caller may log them).  Both return a static string, or NULL for
  * a shape the entry point rejects; they enqueue nothing.

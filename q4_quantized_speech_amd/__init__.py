@@ -61,6 +61,7 @@ _SIGS = {
     "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_quantize": ([_P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "q4_lmhead_argmax_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "q4_matmul_route": ([_I64, _I64, _I64, _SZ, _P], ctypes.c_char_p),
     "q4_matvec_route": ([_I64, _I64, ctypes.c_int32], ctypes.c_char_p),
     "q4_gguf_open": ([_P, _I64, _P], ctypes.c_int),
@@ -266,6 +267,24 @@ def lmhead_argmax(w_q4: torch.Tensor, x: torch.Tensor, workspace: torch.Tensor |
         _check(lib().q4_lmhead_argmax(_ptr(w_q4), _ptr(x2), _ptr(out_idx), _ptr(out_val), m, n, k,
                                       _ptr(workspace), workspace.numel(), _stream(stream)),
                "q4_lmhead_argmax")
+    return out_idx, out_val
+
+
+def lmhead_argmax_noalloc(w_q4: torch.Tensor, x: torch.Tensor, out_idx: torch.Tensor,
+                          out_val: torch.Tensor | None = None, stream=None):
+    """lmhead_argmax with the library's own scratch: the caller passes the
+    outputs, nothing is allocated (M <= 64; calls on one GPU must be ordered)."""
+    n, k = q4_shape(w_q4)
+    x2 = _as_2d_f32(x, k)
+    m = x2.shape[0]
+    _need_cuda(w_q4, x2, out_idx, out_val)
+    if out_idx.dtype != torch.int32 or out_idx.numel() < m or not out_idx.is_contiguous():
+        raise ValueError("out_idx must be a contiguous int32 tensor of at least M entries")
+    if out_val is not None and (out_val.dtype != torch.float32 or out_val.numel() < m
+                                or not out_val.is_contiguous()):
+        raise ValueError("out_val must be a contiguous float32 tensor of at least M entries")
+    _check(lib().q4_lmhead_argmax_noalloc(_ptr(w_q4), _ptr(x2), _ptr(out_idx), _ptr(out_val), m,
+                                          n, k, _stream(stream)), "q4_lmhead_argmax_noalloc")
     return out_idx, out_val
 
 

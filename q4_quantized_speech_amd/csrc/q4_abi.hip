@@ -144,6 +144,18 @@ const char* q4_matvec_route(int64_t N, int64_t K, int32_t argmax) {
   return matvec_route(N, K, argmax != 0);
 }
 
+q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* out_idx,
+                                   float* out_val, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!w_q4 || !x || !out_idx) return Q4_ERR_NULL;
+  if (M < 1 || M > lmhead_noalloc_max_m() || N < 1 || N >= (int64_t(1) << 31) || !k_ok(K) ||
+      N * K >= (int64_t(1) << 40))
+    return Q4_ERR_SHAPE;
+  if (!aligned16(w_q4) || !aligned16(x) || !aligned16(out_idx) || (out_val && !aligned16(out_val)))
+    return Q4_ERR_ALIGN;
+  return hip_status(launch_lmhead_argmax_noalloc(static_cast<const uint8_t*>(w_q4), x, out_idx,
+                                                 out_val, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 q4_status q4_quantize(const float* w, void* w_q4, int64_t N, int64_t K, int32_t* flag,
                       void* stream) {
   if (!w || !w_q4) return Q4_ERR_NULL;

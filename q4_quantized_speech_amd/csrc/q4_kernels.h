@@ -18,6 +18,12 @@ hipError_t launch_matvec(const uint8_t* w, const float* x, float* y, int64_t M, 
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,
                                 int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t s);
 size_t lmhead_workspace_bytes(int64_t M);
+// The argmax with the library's own per-device scratch (no allocation);
+// 1 <= M <= lmhead_noalloc_max_m().
+int64_t lmhead_noalloc_max_m();
+hipError_t launch_lmhead_argmax_noalloc(const uint8_t* w, const float* x, int32_t* out_idx,
+                                        float* out_val, int64_t M, int64_t N, int64_t K,
+                                        hipStream_t s);
 // Name of the matvec kernel variant launched for (N, K) (argmax or not).
 const char* matvec_route(int64_t N, int64_t K, bool argmax);
 // Name of the matmul kernel launched for the shape and workspace size, and

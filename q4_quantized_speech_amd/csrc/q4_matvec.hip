@@ -41,6 +41,8 @@
 // in the workspace with one device-scope atomic max; the last workgroup to
 // arrive writes the result and clears the workspace (no second launch).
 
+#include <mutex>
+
 #include "q4_device.h"
 #include "q4_kernels.h"
 
@@ -566,6 +568,64 @@ size_t lmhead_workspace_bytes(int64_t M) {
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,
                                 int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t s) {
   return launch_mv<true>(w, x, nullptr, out_idx, out_val, workspace, M, N, K, s);
+}
+
+// ---------------------------------------------------------------------------
+// The argmax for callers that cannot allocate: its workspace (the per-row
+// key and arrival counter, zero between calls) is this file-scope array,
+// one copy per GPU, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address
+// comes from hipGetSymbolAddress, taken once per device (with that device
+// current) at the first call there, and only that address is passed on.
+// The first call on a device also clears the array with a fill kernel on
+// its stream; every completed call leaves it zero again.
+// ---------------------------------------------------------------------------
+constexpr int NOALLOC_MAX_M = 64;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_MAX_M * AM_ROW_BYTES];
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+namespace {
+constexpr int kNoallocDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoallocDevices];   // device address of `scratch`, per device
+bool g_scratch_cleared[kNoallocDevices];
+}  // namespace
+
+int64_t lmhead_noalloc_max_m() { return NOALLOC_MAX_M; }
+
+hipError_t launch_lmhead_argmax_noalloc(const uint8_t* w, const float* x, int32_t* out_idx,
+                                        float* out_val, int64_t M, int64_t N, int64_t K,
+                                        hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoallocDevices) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (ptr == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev] = ptr;
+    }
+    ptr = g_scratch_ptr[dev];
+    clear = !g_scratch_cleared[dev];
+    g_scratch_cleared[dev] = true;
+  }
+  if (clear) {
+    const int words = NOALLOC_MAX_M * AM_ROW_BYTES / 4;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_mv<true>(w, x, nullptr, out_idx, out_val, ptr, M, N, K, s);
 }
 
 }  // namespace q4

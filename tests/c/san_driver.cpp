@@ -33,6 +33,12 @@ hipError_t launch_lmhead_argmax(const uint8_t*, const float*, int32_t*, float*, 
   return hipSuccess;
 }
 size_t lmhead_workspace_bytes(int64_t M) { return static_cast<size_t>(M) * 256; }
+int64_t lmhead_noalloc_max_m() { return 64; }
+hipError_t launch_lmhead_argmax_noalloc(const uint8_t*, const float*, int32_t*, float*, int64_t,
+                                        int64_t, int64_t, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 const char* matvec_route(int64_t, int64_t, bool) { return "stub"; }
 const char* matmul_route(int64_t, int64_t, int64_t, size_t, int, int* splits) {
   if (splits) *splits = 1;
@@ -104,6 +110,11 @@ static int run_abi() {
   EXPECT(q4_lmhead_argmax(buf, buf, idx, nullptr, 2, 4, 32, ws, 256, nullptr), Q4_ERR_WORKSPACE);
   EXPECT(q4_lmhead_argmax(buf, buf, idx, nullptr, 1, 4, 32, nullptr, 256, nullptr), Q4_ERR_WORKSPACE);
   EXPECT(q4_lmhead_argmax(buf, buf, idx, nullptr, 65, 4, 32, ws, sizeof ws, nullptr), Q4_ERR_SHAPE);
+  // q4_lmhead_argmax_noalloc
+  EXPECT(q4_lmhead_argmax_noalloc(buf, buf, idx, buf, 64, 4, 32, nullptr), Q4_OK);
+  EXPECT(q4_lmhead_argmax_noalloc(buf, buf, idx, buf, 65, 4, 32, nullptr), Q4_ERR_SHAPE);
+  EXPECT(q4_lmhead_argmax_noalloc(buf, buf, nullptr, buf, 1, 4, 32, nullptr), Q4_ERR_NULL);
+  EXPECT(q4_lmhead_argmax_noalloc(buf, mis, idx, buf, 1, 4, 32, nullptr), Q4_ERR_ALIGN);
   // q4_quantize
   EXPECT(q4_quantize(buf, ws, 4, 64, idx, nullptr), Q4_OK);
   EXPECT(q4_quantize(buf, ws, 4, 64, reinterpret_cast<int32_t*>(ws + 2), nullptr), Q4_ERR_ALIGN);
@@ -122,6 +133,7 @@ static int run_abi() {
         q4_embed_rows(buf, idx, buf, a, b, c, nullptr);
         q4_lmhead_argmax(buf, buf, idx, buf, a, b, c, ws, sizeof ws, nullptr);
         q4_lmhead_argmax_workspace_bytes(a, b, c);
+        q4_lmhead_argmax_noalloc(buf, buf, idx, buf, a, b, c, nullptr);
         q4_quantize(buf, ws, b, c, nullptr, nullptr);
         q4_row_bytes(c);
       }

@@ -11,8 +11,9 @@ them).
 The same run also measures, each in its own timed loop: the second half of the
 metric (q4_matmul TFLOP/s over the encoder layer at M = 1500 plus the adapter at
 M = 375), the LM-head argmax and embedding gather over the 131072 x 3072 table,
-one greedy decode step as a chain (the four projections, the LM-head argmax
-and the embedding row of the chosen token), small batches (M = 2 .. 15), the
+one greedy decode step as a chain (q4_decode_chain: the four projections,
+each reading the previous one's output, the LM-head argmax and the embedding
+row of the chosen token), small batches (M = 2 .. 15), the
 single 3072 x 3072 matvec, and the prefix GEMMs (M = 16 / 38 / 76).  Kernel
 durations come from HIP events recorded on the launch stream around each
 launch.  The CPU baseline is the oracle (float64 dequantise + BLAS dgemv) on a
@@ -169,22 +170,30 @@ def main():
         del gw
     gt = GraphTimer(torch, stream, layer_step, steps)
     us_step = gt.time_us(1, warmup=0)
-    reps = max(1, -(-steps // r_layer))
     ms_per_step = us_step * 1e-3
     value_gbs = layer_bytes / (us_step * 1e-6) / 1e9
     log(f"decode step {us_step:.2f} us -> {value_gbs:.1f} GB/s ({steps} steps)")
     del gt
 
-    # per-launch durations of each projection: a graph of its rotated launches
+    def timed(fn, n, min_launches=200):
+        """Mean microseconds per launch: a graph of at least `min_launches`
+        launches (the rotation of n weight copies repeated), so the boundary
+        between graph replays adds little per launch; at least ~400 untimed
+        launches first (replays over freshly cloned weight copies, the LM
+        head's 1.1 GB above all, run slow for a while)."""
+        n_graph = n * max(1, -(-min_launches // n))
+        g = GraphTimer(torch, stream, fn, n_graph)
+        us = g.time_us(max(3, 800 // n_graph), warmup=max(2, 400 // n_graph))
+        del g
+        return us
+
+    # per-launch durations of each projection: graphs of its rotated launches
     per_proj = {}
     for j, (name, n, k, _, x, y) in enumerate(layer):
-        g = GraphTimer(torch, stream,
-                       lambda i, j=j, x=x, y=y: q4.matvec(copies[i % r_layer][j], x, out=y, stream=stream),
-                       r_layer)
-        us = g.time_us(max(4, reps // 2))
+        us = timed(lambda i, j=j, x=x, y=y: q4.matvec(copies[i % r_layer][j], x, out=y, stream=stream),
+                   r_layer)
         per_proj[name] = {"us": round(us, 3), "gbs": round(weight_bytes(n, k) / (us * 1e-6) / 1e9, 1),
                           "frac_hbm": round(weight_bytes(n, k) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del g
     dominant = max(per_proj, key=lambda nm: per_proj[nm]["us"])
     dn, dk = [(n, k) for (nm, n, k, *_rest) in layer if nm == dominant][0]
     dom_bytes = weight_bytes(dn, dk)
@@ -216,12 +225,9 @@ def main():
             raise RuntimeError("read probe launch failed")
         best = None
         for grid in (512, 1024, 2048, 4096):
-            g = GraphTimer(torch, stream,
-                           lambda i, grid=grid: probe.q4probe_read(bufs[i % r].data_ptr(), nbytes, grid,
-                                                                  sink.data_ptr(), stream.cuda_stream),
-                           r)
-            us = g.time_us(max(4, reps // 2))
-            del g
+            us = timed(lambda i, grid=grid: probe.q4probe_read(bufs[i % r].data_ptr(), nbytes, grid,
+                                                              sink.data_ptr(), stream.cuda_stream),
+                       r, min_launches=200 if nbytes < (64 << 20) else 16)
             if best is None or us < best[0]:
                 best = (us, grid)
         del bufs
@@ -238,14 +244,6 @@ def main():
         roofline["frac_of_ceiling"] = round(achieved / ceil_dom["gbs"], 4)
     else:
         log("libq4probe.so not built: no measured read ceiling")
-
-    def timed(fn, n):
-        # at least ~400 untimed launches first: replays over freshly cloned
-        # weight copies (the LM head's 1.1 GB above all) run slow for a while
-        g = GraphTimer(torch, stream, fn, n)
-        us = g.time_us(max(3, 200 // n), warmup=max(10, 400 // n))
-        del g
-        return us
 
     # ---------------- single 3072 x 3072 matvec ----------------
     n = k = 3072
@@ -278,23 +276,31 @@ def main():
     us = timed(lambda i: q4.embed_rows(tables[i % rt], ids, out=emb, stream=stream), rt)
     rows["embed_rows_38x3072"] = {"us": round(us, 3)}
 
-    # ---------------- one greedy decode step as a chain ----------------
-    # the four projections, the LM-head argmax and the embedding row of the
-    # chosen token (its id read from device memory), back to back on one
-    # stream; weights rotated over the layer and table copies
-    emb1 = torch.empty((1, D), device="cuda")
+    # ---------------- one greedy decode step as a chain (q4_decode_chain) ----------------
+    # the four projections, each reading a slice of the previous one's output
+    # (QKV -> O reads the first 4096 outputs, where attention would be;
+    # gate+up -> down the first 9216, where the gated activation would be),
+    # then the LM-head argmax over the down projection's output and the
+    # chosen token's embedding row, in one call; weights rotated over the
+    # layer and table copies
+    emb1 = torch.empty(D, device="cuda")
+    x0 = layer[0][4]
+    ys = [y for (_, _, _, _, _, y) in layer]
+    chain_x = [x0, ys[0][:4096], ys[1], ys[2][:9216]]
 
     def chain_step(i):
-        layer_step(i)
-        q4.lmhead_argmax(tables[i % rt], xl, workspace=ws, out_idx=oi, out_val=ov, stream=stream)
-        q4.embed_rows(tables[i % rt], oi, out=emb1, stream=stream)
+        steps = [(copies[i % r_layer][j], chain_x[j], ys[j]) for j in range(len(layer))]
+        q4.decode_chain(steps, table_q4=tables[i % rt], head_x=ys[3], out_idx=oi, out_val=ov,
+                        out_embed=emb1, workspace=ws, stream=stream)
 
     us = timed(chain_step, max(r_layer, rt))
     chain_bytes = layer_bytes + weight_bytes(V, D) + weight_bytes(1, D)
     rows["decode_chain_layer_lmhead_embed"] = {
         "us": round(us, 3), "gbs": round(chain_bytes / (us * 1e-6) / 1e9, 1),
         "frac_hbm": round(chain_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "bytes": chain_bytes}
+        "bytes": chain_bytes, "launches": 5,
+        "entry_point": "q4_decode_chain (4 dependent matvec steps + argmax with the chosen "
+                       "token's embedding row in the same launch)"}
     del tables, table
 
     # ---------------- small batches: M = 2 .. 15 over the decoder layer ----------------

@@ -173,6 +173,51 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * q4_decode_chain -- one greedy decode step's Q4_0 work as one call (section
+ * "Architecture": the decoder of width 3072 runs its projections once per
+ * generated token, the LM head picks the token; section "Solutions
+ * techniques pour l'exécution dans le navigateur", item 3: the 131072-row
+ * table in Q4 gives both the logits and the next token's embedding).
+ *   steps[0 .. nsteps-1] : matvecs run in order at M = 1,
+ *                          y[n] = sum_k deq(W)[n, k] x[k]; a step starts
+ *                          reading its x only after every earlier step has
+ *                          written its y, so x may lie inside an earlier y.
+ *                          The array is read during the call only.
+ *   table_q4 (nullable)  : the tied table, vocab rows of dim.  If given, the
+ *                          argmax over deq(T) head_x follows the steps
+ *                          (head_x may lie inside a step's y): out_idx[0]
+ *                          = the lowest index of the maximum, out_val[0]
+ *                          (nullable) the maximum, and out_embed (nullable,
+ *                          dim floats) = deq(T[out_idx[0]]) -- the next
+ *                          step's input, decoded by the argmax's last
+ *                          workgroup in the same launch (zeros if no logit
+ *                          is a number).
+ *   workspace, ws_bytes  : as for q4_lmhead_argmax with M = 1 (256 bytes,
+ *                          zero before the first call, left zero); needed
+ *                          only with a table.
+ *   0 <= nsteps <= Q4_CHAIN_MAX_STEPS; nsteps == 0 needs a table.
+ * Same arithmetic and bounds as q4_matvec and q4_lmhead_argmax; every
+ * argument is validated before anything is enqueued.  One launch per step
+ * and one for the argmax and embedding, all on `stream`: on this chip a
+ * kernel boundary (~2 us) orders the steps at less cost than a grid-wide
+ * barrier inside one persistent kernel (measured 3.8 us with relaxed
+ * atomics over 256 workgroups, 7.3 us with the release and acquire that the
+ * memory model requires for the step's outputs to be visible).
+ */
+#define Q4_CHAIN_MAX_STEPS 64
+typedef struct q4_matvec_step {
+  const void* w_q4;  /* N rows of Q4_0, N*18*K/32 bytes (device)           */
+  const float* x;    /* K floats (device)                                  */
+  float* y;          /* N floats (device), written                         */
+  int64_t N;
+  int64_t K;
+} q4_matvec_step;
+q4_status q4_decode_chain(const q4_matvec_step* steps, int64_t nsteps, const void* table_q4,
+                          int64_t vocab, int64_t dim, const float* head_x, int32_t* out_idx,
+                          float* out_val, float* out_embed, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/*
  * q4_lmhead_argmax_noalloc -- q4_lmhead_argmax for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments and results as

@@ -62,6 +62,7 @@ _SIGS = {
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_quantize": ([_P, _P, _I64, _I64, _P, _P], ctypes.c_int),
     "q4_lmhead_argmax_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "q4_decode_chain": ([_P, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "q4_matmul_route": ([_I64, _I64, _I64, _SZ, _P], ctypes.c_char_p),
     "q4_matvec_route": ([_I64, _I64, ctypes.c_int32], ctypes.c_char_p),
     "q4_gguf_open": ([_P, _I64, _P], ctypes.c_int),
@@ -268,6 +269,50 @@ def lmhead_argmax(w_q4: torch.Tensor, x: torch.Tensor, workspace: torch.Tensor |
                                       _ptr(workspace), workspace.numel(), _stream(stream)),
                "q4_lmhead_argmax")
     return out_idx, out_val
+
+
+class _Step(ctypes.Structure):
+    _fields_ = [("w_q4", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def decode_chain(steps, table_q4: torch.Tensor | None = None, head_x: torch.Tensor | None = None,
+                 out_idx: torch.Tensor | None = None, out_val: torch.Tensor | None = None,
+                 out_embed: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None):
+    """One decode step's Q4_0 work in order on one stream: ``steps`` is a list
+    of (w_q4, x, y) matvecs at M = 1 (x may be a view into an earlier y), then,
+    with ``table_q4``, the argmax over deq(T) head_x and, with ``out_embed``,
+    the chosen token's decoded row.  Returns (out_idx, out_val, out_embed)."""
+    arr = (_Step * max(1, len(steps)))()
+    keep = []
+    for i, (w, x, y) in enumerate(steps):
+        n, k = q4_shape(w)
+        if x.dtype != torch.float32 or x.dim() != 1 or x.shape[0] != k or not x.is_contiguous():
+            raise ValueError(f"step {i}: x must be a contiguous float32 vector of {k}")
+        if y.dtype != torch.float32 or y.dim() != 1 or y.shape[0] != n or not y.is_contiguous():
+            raise ValueError(f"step {i}: y must be a contiguous float32 vector of {n}")
+        _need_cuda(w, x, y)
+        arr[i] = _Step(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
+        keep.append((w, x, y))
+    vocab = dim = 0
+    with _on(stream):
+        if table_q4 is not None:
+            vocab, dim = q4_shape(table_q4)
+            if head_x is None or head_x.dtype != torch.float32 or head_x.numel() != dim \
+                    or not head_x.is_contiguous():
+                raise ValueError(f"head_x must be a contiguous float32 vector of {dim}")
+            if workspace is None:
+                workspace = lmhead_workspace(1, head_x.device)
+            if out_idx is None:
+                out_idx = torch.empty(1, dtype=torch.int32, device=head_x.device)
+            _need_cuda(table_q4, head_x, out_idx, out_val, out_embed, workspace)
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        _check(lib().q4_decode_chain(ctypes.cast(arr, ctypes.c_void_p), len(steps), _ptr(table_q4),
+                                     vocab, dim, _ptr(head_x), _ptr(out_idx), _ptr(out_val),
+                                     _ptr(out_embed), _ptr(workspace), ws_bytes, _stream(stream)),
+               "q4_decode_chain")
+    return out_idx, out_val, out_embed
 
 
 def lmhead_argmax_noalloc(w_q4: torch.Tensor, x: torch.Tensor, out_idx: torch.Tensor,

@@ -127,8 +127,9 @@ q4_status q4_lmhead_argmax(const void* w_q4, const float* x, int32_t* out_idx, f
     return Q4_ERR_ALIGN;
   if (!workspace || ws_bytes < lmhead_workspace_bytes(M)) return Q4_ERR_WORKSPACE;
   if (!aligned16(workspace)) return Q4_ERR_ALIGN;
-  return hip_status(launch_lmhead_argmax(static_cast<const uint8_t*>(w_q4), x, out_idx, out_val, M,
-                                         N, K, workspace, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_lmhead_argmax(static_cast<const uint8_t*>(w_q4), x, out_idx, out_val,
+                                         nullptr, M, N, K, workspace,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 const char* q4_matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int32_t* splits) {
@@ -142,6 +143,42 @@ const char* q4_matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, in
 const char* q4_matvec_route(int64_t N, int64_t K, int32_t argmax) {
   if (N < 1 || N >= (int64_t(1) << 31) || !k_ok(K) || N * K >= (int64_t(1) << 40)) return nullptr;
   return matvec_route(N, K, argmax != 0);
+}
+
+q4_status q4_decode_chain(const q4_matvec_step* steps, int64_t nsteps, const void* table_q4,
+                          int64_t vocab, int64_t dim, const float* head_x, int32_t* out_idx,
+                          float* out_val, float* out_embed, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  if (nsteps < 0 || nsteps > Q4_CHAIN_MAX_STEPS) return Q4_ERR_SHAPE;
+  if (nsteps > 0 && !steps) return Q4_ERR_NULL;
+  if (nsteps == 0 && !table_q4) return Q4_ERR_SHAPE;  // nothing to do
+  for (int64_t i = 0; i < nsteps; ++i) {
+    const q4_matvec_step& st = steps[i];
+    if (!st.w_q4 || !st.x || !st.y) return Q4_ERR_NULL;
+    if (st.N < 1 || st.N >= (int64_t(1) << 31) || !k_ok(st.K) || st.N * st.K >= (int64_t(1) << 40))
+      return Q4_ERR_SHAPE;
+    if (!aligned16(st.w_q4) || !aligned16(st.x) || !aligned16(st.y)) return Q4_ERR_ALIGN;
+  }
+  if (table_q4) {
+    if (!head_x || !out_idx) return Q4_ERR_NULL;
+    if (vocab < 1 || vocab >= (int64_t(1) << 31) || !k_ok(dim) || vocab * dim >= (int64_t(1) << 40))
+      return Q4_ERR_SHAPE;
+    if (!aligned16(table_q4) || !aligned16(head_x) || !aligned16(out_idx) ||
+        (out_val && !aligned16(out_val)) || (out_embed && !aligned16(out_embed)))
+      return Q4_ERR_ALIGN;
+    if (!workspace || ws_bytes < lmhead_workspace_bytes(1)) return Q4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t i = 0; i < nsteps; ++i) {
+    const q4_matvec_step& st = steps[i];
+    const hipError_t e = launch_matvec(static_cast<const uint8_t*>(st.w_q4), st.x, st.y, 1, st.N,
+                                       st.K, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!table_q4) return Q4_OK;
+  return hip_status(launch_lmhead_argmax(static_cast<const uint8_t*>(table_q4), head_x, out_idx,
+                                         out_val, out_embed, 1, vocab, dim, workspace, s));
 }
 
 q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* out_idx,

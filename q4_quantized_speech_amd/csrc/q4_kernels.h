@@ -15,8 +15,10 @@ DeviceInfo device_info();
 hipError_t launch_matvec(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, hipStream_t s);
 
+// out_embed (nullable): the decoded table row of each chosen index, [M, K].
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,
-                                int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t s);
+                                float* out_embed, int64_t M, int64_t N, int64_t K, void* workspace,
+                                hipStream_t s);
 size_t lmhead_workspace_bytes(int64_t M);
 // The argmax with the library's own per-device scratch (no allocation);
 // 1 <= M <= lmhead_noalloc_max_m().

@@ -163,13 +163,47 @@ __device__ __forceinline__ uint64_t am_key(float v, int i) {
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
 }
+// The chosen token's row of the (tied) table, decoded by the whole
+// workgroup: out[0..K) = deq(W[idx]), zeros when there is no candidate.
+__device__ __forceinline__ void am_embed_row(const uint8_t* __restrict__ W, int idx, int64_t N,
+                                             int K, float* __restrict__ out) {
+  const int nb = K / QK;
+  for (int b = static_cast<int>(threadIdx.x); b < nb; b += static_cast<int>(blockDim.x)) {
+    f32x4* dst = reinterpret_cast<f32x4*>(out + static_cast<int64_t>(b) * QK);
+    if (idx < 0 || idx >= N) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dst[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      continue;
+    }
+    uint32_t d16, qs[4];
+    load_block_any(W, static_cast<int64_t>(idx) * nb + b, d16, qs);
+    const float d = half_bits_to_float(d16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = qs[u] & 0x0F0F0F0Fu;
+      const uint32_t hi = (qs[u] >> 4) & 0x0F0F0F0Fu;
+      dst[u] = f32x4{(ubyte_f<0>(lo) - 8.f) * d, (ubyte_f<1>(lo) - 8.f) * d,
+                     (ubyte_f<2>(lo) - 8.f) * d, (ubyte_f<3>(lo) - 8.f) * d};
+      dst[4 + u] = f32x4{(ubyte_f<0>(hi) - 8.f) * d, (ubyte_f<1>(hi) - 8.f) * d,
+                         (ubyte_f<2>(hi) - 8.f) * d, (ubyte_f<3>(hi) - 8.f) * d};
+    }
+  }
+}
+
+// emb (nullable): where the last workgroup of row m also writes the decoded
+// table row of the chosen index (K floats at emb + m K), so the next decode
+// step's input needs no second launch.
 __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* workspace, int nwg,
-                                           int32_t* out_idx, float* out_val) {
+                                           int32_t* out_idx, float* out_val,
+                                           const uint8_t* __restrict__ W, float* emb, int64_t N,
+                                           int K) {
+  __shared__ int s_chosen;  // the index, in the last workgroup; -2 in the others
   char* row = reinterpret_cast<char*>(workspace) + static_cast<int64_t>(m) * AM_ROW_BYTES;
   uint64_t* key = reinterpret_cast<uint64_t*>(row);
   uint32_t* count = reinterpret_cast<uint32_t*>(row + 128);
   am_block_reduce(bv, bi);
   if (threadIdx.x == 0) {
+    s_chosen = -2;
     const uint64_t mine = am_key(bv, bi);
     const uint64_t old = __hip_atomic_fetch_max(key, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t prev;
@@ -191,7 +225,13 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
       }
       out_idx[m] = idx;
       if (out_val) out_val[m] = val;
+      s_chosen = idx;
     }
+  }
+  if (emb != nullptr) {  // the same in every thread
+    __syncthreads();
+    const int idx = s_chosen;
+    if (idx != -2) am_embed_row(W, idx, N, K, emb + static_cast<int64_t>(m) * K);
   }
 }
 
@@ -389,7 +429,8 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     load(row0 + stride, wb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (ARGMAX) am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val);
+  if constexpr (ARGMAX)
+    am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val, W, Y, N, K);
 }
 
 // Generic kernel: any K % 32 == 0 (odd block counts, very long rows).  16
@@ -429,7 +470,8 @@ __global__ __launch_bounds__(256) void matvec_any_kernel(
       if (ok && j == 0) Y[static_cast<int64_t>(m) * N + row] = v;
     }
   }
-  if constexpr (ARGMAX) am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val);
+  if constexpr (ARGMAX)
+    am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val, W, Y, N, K);
 }
 
 // Grid of the pair kernel with R rows per lane: the fewest passes per
@@ -566,8 +608,10 @@ size_t lmhead_workspace_bytes(int64_t M) {
 }
 
 hipError_t launch_lmhead_argmax(const uint8_t* w, const float* x, int32_t* out_idx, float* out_val,
-                                int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t s) {
-  return launch_mv<true>(w, x, nullptr, out_idx, out_val, workspace, M, N, K, s);
+                                float* out_embed, int64_t M, int64_t N, int64_t K, void* workspace,
+                                hipStream_t s) {
+  // in the argmax kernels the output pointer Y carries the embedding rows
+  return launch_mv<true>(w, x, out_embed, out_idx, out_val, workspace, M, N, K, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,13 +1,15 @@
 """Profiling driver: runs one benchmark workload eagerly, for rocprofv3.
 
-    python -m q4_quantized_speech_amd.profile_driver run WORKLOAD [--iters N]
+    python -m q4_quantized_speech_amd.profile_driver run WORKLOAD [--iters N] [--graph]
     python -m q4_quantized_speech_amd.profile_driver traffic WORKLOAD \
         --fetch FETCH.csv --write WRITE.csv [--out FILE]
     python -m q4_quantized_speech_amd.profile_driver trace KERNEL_TRACE.csv [--out FILE]
 
 ``run`` builds the inputs of one workload with the same seeds and shapes as
 bench.py, rotates enough weight copies (>= 1 GiB) that the Infinity Cache
-cannot serve them, and calls the library N times; it then runs a plain
+cannot serve them, and calls the library N times, eagerly or (``--graph``)
+as replays of one HIP graph of the rotated calls, which is how bench.py
+times them (it then prints the mean per call from HIP events); it then runs a plain
 element-wise kernel over 256 MiB (``torch.neg``: 256 MiB read, 256 MiB
 written) whose counter readings calibrate the HBM counters.
 
@@ -24,6 +26,7 @@ tells them apart).
 
 Workload names are the keys bench.py reports:
     matvec_{qkv,o,gate_up,down}      decoder projections at M = 1
+    decode_step                      the four of them back to back
     matvec_3072x3072                 the single matvec
     lmhead_argmax_131072x3072        LM-head argmax at M = 1
     embed_rows_38x3072               embedding gather of 38 ids
@@ -93,7 +96,7 @@ def dispatches_per_call(workload: str) -> int:
 
 # ----------------------------------------------------------------------------- run
 
-def _run(workload: str, iters: int) -> None:
+def _run(workload: str, iters: int, graph: bool = False) -> None:
     import torch
 
     import q4_quantized_speech_amd as q4
@@ -102,6 +105,7 @@ def _run(workload: str, iters: int) -> None:
     dev = "cuda"
     torch.cuda.set_device(0)
     q4.lib()
+    s = torch.cuda.Stream()
 
     def encode(n, k, seed):
         w = torch.from_numpy(synth.weights(n, k, seed)).to(dev)
@@ -109,9 +113,11 @@ def _run(workload: str, iters: int) -> None:
         del w
         return out
 
+    def copies(nbytes):
+        return max(2, -(-CACHE_DEFEAT_BYTES // nbytes))
+
     def rotate(w):
-        r = max(2, -(-CACHE_DEFEAT_BYTES // w.numel()))
-        return [w] + [w.clone() for _ in range(r - 1)]
+        return [w] + [w.clone() for _ in range(copies(w.numel()) - 1)]
 
     def act(m, k, seed):
         return torch.from_numpy(synth.activations(m, k, seed)).to(dev)
@@ -124,22 +130,38 @@ def _run(workload: str, iters: int) -> None:
         ws = rotate(encode(n, k, synth.seed_for(1, t)))
         x = act(1, k, synth.seed_for(1, 10 + t))[0]
         y = torch.empty(n, device=dev)
-        call = lambda i: q4.matvec(ws[i % len(ws)], x, out=y)  # noqa: E731
+        call = lambda i: q4.matvec(ws[i % len(ws)], x, out=y, stream=s)  # noqa: E731
+    elif workload == "decode_step":
+        # the four projections of a decoder layer at M = 1, back to back,
+        # weights rotated as one set (the bench's decode step)
+        layer = [(n, k, encode(n, k, synth.seed_for(1, t)),
+                  act(1, k, synth.seed_for(1, 10 + t))[0], torch.empty(n, device=dev))
+                 for t, (_, n, k) in enumerate(synth.DECODER_LAYER)]
+        nb = sum(weight_bytes(n, k) for (n, k, *_r) in layer)
+        ws = [[w for (_, _, w, _, _) in layer]]
+        ws += [[w.clone() for w in ws[0]] for _ in range(copies(nb) - 1)]
+
+        def call(i):
+            for j, (_, _, _, x, y) in enumerate(layer):
+                q4.matvec(ws[i % len(ws)][j], x, out=y, stream=s)
     elif workload == "matvec_3072x3072":
         ws = rotate(encode(3072, 3072, synth.seed_for(0, 0)))
         x = act(1, 3072, synth.seed_for(0, 1))[0]
         y = torch.empty(3072, device=dev)
-        call = lambda i: q4.matvec(ws[i % len(ws)], x, out=y)  # noqa: E731
+        call = lambda i: q4.matvec(ws[i % len(ws)], x, out=y, stream=s)  # noqa: E731
     elif workload in ("lmhead_argmax_131072x3072", "embed_rows_38x3072"):
         ws = rotate(encode(synth.VOCAB, synth.DEC_DIM, synth.seed_for(2, 0)))
         if workload.startswith("lmhead"):
             x = act(1, synth.DEC_DIM, synth.seed_for(2, 1))
             wsp = q4.lmhead_workspace(1, dev)
-            call = lambda i: q4.lmhead_argmax(ws[i % len(ws)], x, workspace=wsp)  # noqa: E731
+            oi = torch.empty(1, dtype=torch.int32, device=dev)
+            ov = torch.empty(1, device=dev)
+            call = lambda i: q4.lmhead_argmax(ws[i % len(ws)], x, workspace=wsp,  # noqa: E731
+                                              out_idx=oi, out_val=ov, stream=s)
         else:
             ids = torch.from_numpy(synth.token_ids(synth.PREFIX_TOKENS, synth.seed_for(2, 2))).to(dev)
             out = torch.empty((synth.PREFIX_TOKENS, synth.DEC_DIM), device=dev)
-            call = lambda i: q4.embed_rows(ws[i % len(ws)], ids, out=out)  # noqa: E731
+            call = lambda i: q4.embed_rows(ws[i % len(ws)], ids, out=out, stream=s)  # noqa: E731
     else:
         m = re.fullmatch(r"matmul_([a-z_]+)_M(\d+)_(\d+)x(\d+)", workload)
         if not m:
@@ -155,12 +177,45 @@ def _run(workload: str, iters: int) -> None:
         x = act(mm, k, synth.seed_for(cfg, 10 + t))
         y = torch.empty((mm, n), device=dev)
         wsp = q4.matmul_workspace(mm, n, k, dev)
-        call = lambda i: q4.matmul(ws[i % len(ws)], x, out=y, workspace=wsp)  # noqa: E731
+        call = lambda i: q4.matmul(ws[i % len(ws)], x, out=y, workspace=wsp,  # noqa: E731
+                                   stream=s)
 
     torch.cuda.synchronize()
-    print(f"[profile] {workload}: {iters} calls", flush=True)
-    for i in range(iters):
-        call(i)
+    r = len(ws)
+    if graph:
+        # the bench's timing mode: one HIP graph of r rotated calls on the
+        # launch stream, replayed; mean per call from HIP events on that
+        # stream over the timed replays
+        with torch.cuda.stream(s):
+            for i in range(min(r, 3)):
+                call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(r):
+                call(i)
+        torch.cuda.synchronize()
+        reps = max(1, -(-iters // r))
+        warm = max(2, 400 // r)
+        print(f"[profile] {workload}: graph of {r} calls, {warm} untimed + {reps} timed replays",
+              flush=True)
+        with torch.cuda.stream(s):
+            for _ in range(warm):
+                g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps):
+                g.replay()
+            b.record(s)
+        b.synchronize()
+        print(f"[profile] HIP events: {a.elapsed_time(b) * 1e3 / (reps * r):.3f} us per call "
+              f"over the {reps * r} timed calls", flush=True)
+        del g
+    else:
+        print(f"[profile] {workload}: {iters} calls", flush=True)
+        with torch.cuda.stream(s):
+            for i in range(iters):
+                call(i)
     torch.cuda.synchronize()
     del ws
     torch.cuda.empty_cache()
@@ -264,12 +319,16 @@ def _short(name: str) -> str:
 
 def _trace(path: str, out: str | None) -> None:
     rows = defaultdict(list)
+    timeline = []
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
-            ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            ns = t1 - t0
             grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
             wg = r.get("Workgroup_Size") or r.get("Workgroup_Size_X", "")
             rows[(_short(r["Kernel_Name"]), grid, wg)].append(ns)
+            if LIB_KERNEL in r["Kernel_Name"] and not any(k in r["Kernel_Name"] for k in SETUP_KERNELS):
+                timeline.append((t0, t1, _short(r["Kernel_Name"])))
     lines = []
     stats = path.replace("_kernel_trace.csv", "_kernel_stats.csv")
     if stats != path and os.path.exists(stats):  # rocprofv3 --stats of the same run
@@ -287,6 +346,19 @@ def _trace(path: str, out: str | None) -> None:
         v = sorted(v)
         lines.append(f"{k[:58]:58s} {g:>10s} {w:>4s} {len(v):7d} {sum(v) / len(v) / 1e3:9.3f} "
                      f"{v[len(v) // 2] / 1e3:9.3f} {v[0] / 1e3:8.3f}")
+    if len(timeline) > 1:
+        # idle time between one library kernel's end and the next one's start
+        timeline.sort()
+        gaps = defaultdict(list)
+        for (a0, a1, an), (b0, b1, bn) in zip(timeline, timeline[1:]):
+            gaps[(an, bn)].append(b0 - a1)
+        lines.append("## gaps between consecutive library kernels (next start - previous end)")
+        lines.append(f"{'previous kernel -> next kernel':90s} {'count':>6s} {'median_us':>9s} "
+                     f"{'min_us':>8s}")
+        for (an, bn), v in sorted(gaps.items(), key=lambda kv: -len(kv[1])):
+            v = sorted(v)
+            lines.append(f"{(an[:44] + ' -> ' + bn[:42]):90s} {len(v):6d} {v[len(v) // 2] / 1e3:9.3f} "
+                         f"{v[0] / 1e3:8.3f}")
     text = "\n".join(lines) + "\n"
     if out:
         with open(out, "w") as fh:
@@ -300,6 +372,8 @@ def main(argv=None):
     r = sub.add_parser("run")
     r.add_argument("workload")
     r.add_argument("--iters", type=int, default=20)
+    r.add_argument("--graph", action="store_true",
+                   help="replay a HIP graph of rotated calls (the bench's timing mode)")
     t = sub.add_parser("traffic")
     t.add_argument("workload")
     t.add_argument("--fetch", required=True)
@@ -310,7 +384,7 @@ def main(argv=None):
     s.add_argument("--out")
     a = p.parse_args(argv)
     if a.cmd == "run":
-        _run(a.workload, a.iters)
+        _run(a.workload, a.iters, a.graph)
     elif a.cmd == "traffic":
         _traffic(a.workload, a.fetch, a.write, a.out)
     else:

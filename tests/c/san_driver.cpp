@@ -27,8 +27,8 @@ hipError_t launch_matvec(const uint8_t*, const float*, float*, int64_t, int64_t,
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_lmhead_argmax(const uint8_t*, const float*, int32_t*, float*, int64_t, int64_t,
-                                int64_t, void*, hipStream_t) {
+hipError_t launch_lmhead_argmax(const uint8_t*, const float*, int32_t*, float*, float*, int64_t,
+                                int64_t, int64_t, void*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
@@ -115,6 +115,37 @@ static int run_abi() {
   EXPECT(q4_lmhead_argmax_noalloc(buf, buf, idx, buf, 65, 4, 32, nullptr), Q4_ERR_SHAPE);
   EXPECT(q4_lmhead_argmax_noalloc(buf, buf, nullptr, buf, 1, 4, 32, nullptr), Q4_ERR_NULL);
   EXPECT(q4_lmhead_argmax_noalloc(buf, mis, idx, buf, 1, 4, 32, nullptr), Q4_ERR_ALIGN);
+  // q4_decode_chain
+  {
+    q4_matvec_step st[3] = {{buf, buf, buf, 64, 64}, {buf, buf, buf, 3072, 4096},
+                            {buf, buf, buf, 1, 32}};
+    EXPECT(q4_decode_chain(st, 3, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_OK);
+    EXPECT(q4_decode_chain(st, 3, buf, 131072, 3072, buf, idx, buf, buf, ws, 256, nullptr), Q4_OK);
+    EXPECT(q4_decode_chain(st, 0, buf, 10, 64, buf, idx, nullptr, nullptr, ws, 256, nullptr), Q4_OK);
+    EXPECT(q4_decode_chain(st, 0, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_ERR_SHAPE);
+    EXPECT(q4_decode_chain(nullptr, 2, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_ERR_NULL);
+    EXPECT(q4_decode_chain(st, 65, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_ERR_SHAPE);
+    EXPECT(q4_decode_chain(st, 3, buf, 131072, 3072, buf, idx, buf, buf, nullptr, 0, nullptr),
+           Q4_ERR_WORKSPACE);
+    EXPECT(q4_decode_chain(st, 3, buf, 131072, 3072, buf, idx, buf, const_cast<float*>(mis), ws,
+                           256, nullptr), Q4_ERR_ALIGN);
+    q4_matvec_step bad[2] = {{buf, buf, buf, 64, 64}, {buf, buf, buf, 64, 48}};
+    EXPECT(q4_decode_chain(bad, 2, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_ERR_SHAPE);
+    bad[1].K = 64;
+    bad[1].y = nullptr;
+    EXPECT(q4_decode_chain(bad, 2, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr), Q4_ERR_NULL);
+    for (int64_t a : sizes)
+      for (int64_t b : sizes) {
+        q4_matvec_step one = {buf, buf, buf, a, b};
+        q4_decode_chain(&one, 1, buf, a, b, buf, idx, buf, buf, ws, sizeof ws, nullptr);
+      }
+  }
   // q4_quantize
   EXPECT(q4_quantize(buf, ws, 4, 64, idx, nullptr), Q4_OK);
   EXPECT(q4_quantize(buf, ws, 4, 64, reinterpret_cast<int32_t*>(ws + 2), nullptr), Q4_ERR_ALIGN);

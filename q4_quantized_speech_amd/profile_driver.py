@@ -31,6 +31,8 @@ Workload names are the keys bench.py reports:
     lmhead_argmax_131072x3072        LM-head argmax at M = 1
     embed_rows_38x3072               embedding gather of 38 ids
     matmul_<proj>_M<m>_<n>x<k>       encoder, adapter or prefix GEMMs
+    encoder_layer_M<m>               the encoder projections at M and the adapter at M / 4
+    prefix_layer_M<m>                the decoder projections at a prefix of M tokens
 """
 
 from __future__ import annotations
@@ -144,6 +146,27 @@ def _run(workload: str, iters: int, graph: bool = False) -> None:
         def call(i):
             for j, (_, _, _, x, y) in enumerate(layer):
                 q4.matvec(ws[i % len(ws)][j], x, out=y, stream=s)
+    elif re.fullmatch(r"encoder_layer_M\d+", workload) or re.fullmatch(r"prefix_layer_M\d+", workload):
+        # every projection of the encoder layer (+ the adapter at M / 4), or
+        # of the decoder layer at a prefix length, back to back
+        mm = int(workload.rsplit("M", 1)[1])
+        if workload.startswith("encoder"):
+            shapes = [(nm, n, k, mm // 4 if nm == "adapter" else mm, 4, t)
+                      for t, (nm, n, k) in enumerate(list(synth.ENCODER_LAYER) + [synth.ADAPTER])]
+        else:
+            shapes = [(nm, n, k, mm, 3, t) for t, (nm, n, k) in enumerate(synth.DECODER_LAYER)]
+        mats = []
+        for (nm, n, k, m_, cfg, t) in shapes:
+            w0 = encode(n, k, synth.seed_for(cfg, t))
+            mats.append((w0, act(m_, k, synth.seed_for(cfg, 10 + t)),
+                         torch.empty((m_, n), device=dev), q4.matmul_workspace(m_, n, k, dev)))
+        nb = sum(w0.numel() for (w0, *_r) in mats)
+        ws = [[w0 for (w0, *_r) in mats]]
+        ws += [[w0.clone() for w0 in ws[0]] for _ in range(copies(nb) - 1)]
+
+        def call(i):
+            for j, (_, x, y, wsp) in enumerate(mats):
+                q4.matmul(ws[i % len(ws)][j], x, out=y, workspace=wsp, stream=s)
     elif workload == "matvec_3072x3072":
         ws = rotate(encode(3072, 3072, synth.seed_for(0, 0)))
         x = act(1, 3072, synth.seed_for(0, 1))[0]
@@ -310,6 +333,37 @@ def _traffic(workload: str, fetch: str, write: str, out: str) -> None:
         print(f"  WRITE_SIZE {v:.1f} KiB x{c}  {k[:100]}")
 
 
+# ----------------------------------------------------------------------------- counters
+
+def _counters(path: str, out: str | None) -> None:
+    """Per library kernel (and grid): mean of each counter per dispatch, and
+    the MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024
+    SIMDs) where both were collected (the figure rocprofv3 calls MfmaUtil)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if LIB_KERNEL not in r["Kernel_Name"] or any(k in r["Kernel_Name"] for k in SETUP_KERNELS):
+                continue
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
+            vals[(_short(r["Kernel_Name"]), grid)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    lines = [f"{'kernel':44s} {'grid':>8s} {'n':>5s} " + " ".join(f"{c[:24]:>24s}" for c in names)
+             + ("  mfma_busy_%" if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(names) else "")]
+    for (k, g), v in sorted(vals.items()):
+        n = max(len(x) for x in v.values())
+        means = {c: sum(x) / len(x) for c, x in v.items()}
+        line = f"{k[:44]:44s} {g:>8s} {n:5d} " + " ".join(f"{means.get(c, float('nan')):24.1f}"
+                                                          for c in names)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
+            line += f"  {100.0 * means['SQ_VALU_MFMA_BUSY_CYCLES'] / (means['GRBM_GUI_ACTIVE'] * 1024):11.1f}"
+        lines.append(line)
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
 # ----------------------------------------------------------------------------- trace
 
 def _short(name: str) -> str:
@@ -382,11 +436,16 @@ def main(argv=None):
     s = sub.add_parser("trace")
     s.add_argument("csv")
     s.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--out")
     a = p.parse_args(argv)
     if a.cmd == "run":
         _run(a.workload, a.iters, a.graph)
     elif a.cmd == "traffic":
         _traffic(a.workload, a.fetch, a.write, a.out)
+    elif a.cmd == "counters":
+        _counters(a.csv, a.out)
     else:
         _trace(a.csv, a.out)
 

@@ -312,20 +312,40 @@ def test_matmul_wide_tiles(m, n, k):
         assert_within(y, ref, b, *MF, f"wide {m}x{n}x{k} ws={ws is not None}")
 
 
-def test_matmul_split_k_stays_in_bounds():
-    """Partial sums stay inside the workspace, results inside Y."""
-    m, n, k = 70, 150, 2048
+def split_canary_workspace(m, n, k, sentinel):
+    """A workspace of the planned size (splits x M x N partial floats)
+    followed by 64 floats, all set to the sentinel.  Returns (ws floats,
+    need bytes)."""
+    need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k))
+    route, splits = q4.matmul_route(m, n, k, need)
+    assert need > 0 and splits > 1 and need == splits * m * n * 4, (route, splits, need)
+    ws = torch.full((need // 4 + 64,), sentinel, dtype=torch.float32, device="cuda")
+    return ws, need
+
+
+@pytest.mark.parametrize("m,n,k", [(70, 150, 2048), (300, 256, 1024), (375, 1280, 1280),
+                                   (1500, 1280, 5120), (40, 3072, 9216)])
+def test_matmul_split_k_stays_in_bounds(m, n, k):
+    """Partial sums stay inside the workspace, results inside Y, every
+    output written, and a second call gives the same bits: the skinny, tile
+    and wide kernels with a K split."""
     qb = dev(O.quantize_q4_0(_rand_w(n, k, 8)))
     x = dev(_rand_x(m, k, 9))
-    need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k))
-    assert need > 0
     sentinel = -12345.0
-    ws = torch.full((need // 4 + 64,), sentinel, dtype=torch.float32, device="cuda")
+    ws, need = split_canary_workspace(m, n, k, sentinel)
     out = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
-    announce("matmul split-K canary")
-    q4.matmul(qb, x, out=out[: m * n].view(m, n), workspace=ws[: need // 4].view(torch.uint8))
-    assert np.all(host(ws)[need // 4:] == sentinel)
-    assert np.all(host(out)[m * n:] == sentinel)
+    announce(f"matmul split-K canary {q4.matmul_route(m, n, k, need)} {m}x{n}x{k}")
+    first = None
+    for rep in range(2):
+        q4.matmul(qb, x, out=out[: m * n].view(m, n), workspace=ws[: need // 4].view(torch.uint8))
+        got = host(out)
+        assert np.all(host(ws)[need // 4:] == sentinel)
+        assert np.all(got[m * n:] == sentinel)
+        assert not np.any(got[: m * n] == sentinel)
+        if first is None:
+            first = got[: m * n].copy()
+        else:
+            assert np.array_equal(got[: m * n].view(np.uint32), first.view(np.uint32))
 
 
 @pytest.mark.parametrize("m", [16, 38, 76])

@@ -16,6 +16,7 @@ import torch
 
 import q4_quantized_speech_amd as q4
 from gpu_util import announce, assert_within, dev, host, needs_gpu, weights_q4
+from test_gpu_parity import split_canary_workspace
 from oracle import q4_oracle as O
 from q4_quantized_speech_amd import synth
 
@@ -119,10 +120,8 @@ def test_small_m_deterministic_and_in_bounds():
     m, n, k = 3, 200, 12352
     qb = dev(_w(n, k, 21))
     x = dev(synth.activations(m, k, 22))
-    need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k))
-    assert need > 0, "a K split is planned for this shape"
     sentinel = -12345.0
-    ws = torch.full((need // 4 + 64,), sentinel, dtype=torch.float32, device="cuda")
+    ws, need = split_canary_workspace(m, n, k, sentinel)
     out = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
     announce("small-M canary")
     q4.matmul(qb, x, out=out[: m * n].view(m, n), workspace=ws[: need // 4].view(torch.uint8))

@@ -83,6 +83,20 @@ def stored_traffic(kernel_key: str):
     return float(v) if v else None
 
 
+def profile_figures(workload: str, work: float, peak_per_us: float):
+    """The committed rocprofv3 kernel trace of `workload` (profiles/, taken in
+    this benchmark's timing mode): its kernel time per call and the fraction
+    of peak it gives, beside the live HIP-event figure; empty if the trace
+    is missing or was taken on other sources."""
+    from q4_quantized_speech_amd.profile_driver import profile_call_us
+    name = f"kernel_trace_{workload}.txt"
+    us = profile_call_us(os.path.join(ROOT, "profiles", name), workload)
+    if us is None:
+        return {"profile": None}
+    return {"profile": {"file": f"profiles/{name}", "kernel_us_per_call": round(us, 3),
+                        "frac": round(work / us / peak_per_us, 4)}}
+
+
 class GraphTimer:
     """Capture `fn(i)` for i in range(n) into one HIP graph on `stream`, then
     time `reps` replays with HIP events recorded on that stream."""
@@ -204,6 +218,7 @@ def main():
                 "kernel": f"q4_matvec {dominant} {dn}x{dk}",
                 "bytes_per_launch": dom_bytes,
                 "launch_us_mean": per_proj[dominant]["us"]}
+    roofline.update(profile_figures(f"matvec_{dominant}", dom_bytes, HBM_PEAK_GBS * 1e3))
     rows = {"decode_layer_projections": per_proj}
 
     # Measured read ceiling: a plain coalesced read kernel (libq4probe.so, not
@@ -356,6 +371,8 @@ def main():
         enc_shapes, lambda nm: m_enc // 4 if nm == "adapter" else m_enc, 4)
     enc_tflops = enc_flop / (enc_us * 1e-6) / 1e12
     dom_gemm = max(enc_rows, key=lambda nm: enc_rows[nm]["us"])
+    _m, _nk = dom_gemm.split("_M")[1].split("_", 1)
+    m_dom, (n_dom, k_dom) = int(_m), map(int, _nk.split("x"))
     matmul = {
         "metric": "q4_matmul TFLOP/s, encoder layer (QKV 3840x1280, O 1280x1280, up 5120x1280, "
                   "down 1280x5120) at M=1500 + adapter 3072x5120 at M=375",
@@ -363,7 +380,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": enc_rows[dom_gemm]["tflops"],
                      "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(enc_rows[dom_gemm]["tflops"] / F16_PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic(f"matmul_{dom_gemm}"), "kernel": f"q4_matmul {dom_gemm}"},
+                     "traffic": stored_traffic(f"matmul_{dom_gemm}"), "kernel": f"q4_matmul {dom_gemm}",
+                     "launch_us_mean": enc_rows[dom_gemm]["us"],
+                     **profile_figures(f"matmul_{dom_gemm}", 2.0 * m_dom * n_dom * k_dom,
+                                       F16_PEAK_TFLOPS * 1e6)},
         "frac_of_peak_whole_layer": round(enc_tflops / F16_PEAK_TFLOPS, 4),
         "per_projection": enc_rows}
     for m in (375, 3000):

@@ -3,7 +3,9 @@
     python -m q4_quantized_speech_amd.profile_driver run WORKLOAD [--iters N] [--graph]
     python -m q4_quantized_speech_amd.profile_driver traffic WORKLOAD \
         --fetch FETCH.csv --write WRITE.csv [--out FILE]
-    python -m q4_quantized_speech_amd.profile_driver trace KERNEL_TRACE.csv [--out FILE]
+    python -m q4_quantized_speech_amd.profile_driver trace KERNEL_TRACE.csv [--out FILE] \
+        [--last N --workload WORKLOAD] [--cmd TEXT ...]
+    python -m q4_quantized_speech_amd.profile_driver counters COUNTERS.csv [--out FILE] [--cmd TEXT ...]
 
 ``run`` builds the inputs of one workload with the same seeds and shapes as
 bench.py, rotates enough weight copies (>= 1 GiB) that the Infinity Cache
@@ -22,7 +24,15 @@ with a hash of its kernels' sources so that stale figures are ignored.
 
 ``trace`` summarises a ``rocprofv3 --kernel-trace`` CSV per kernel and grid
 size (the library launches one kernel template for several shapes; the grid
-tells them apart).
+tells them apart); with ``--last N`` it also gives each library kernel's mean
+over its last N dispatches (the timed window of a ``run --graph``), tagged
+with the workload's source hash, which bench.py reads back.
+
+``counters`` gives, per library kernel and grid, the mean of each counter of
+a ``rocprofv3 --pmc`` run and the MFMA busy fraction.
+
+``--cmd`` lines (repeatable) go at the top of a summary as '# ' comments: the
+commands that produced it.
 
 Workload names are the keys bench.py reports:
     matvec_{qkv,o,gate_up,down}      decoder projections at M = 1
@@ -50,6 +60,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 CACHE_DEFEAT_BYTES = 1 << 30
+XCDS = 8                       # accelerator complex dies of the MI355X (GRBM counter instances)
 CAL_BYTES = 256 << 20          # calibration kernel: reads and writes this many bytes
 CAL_KERNEL = "neg_kernel"      # substring of torch's element-wise negation kernel
 LIB_KERNEL = "q4::"            # namespace of the library's kernels
@@ -67,6 +78,9 @@ KERNEL_SOURCES = {
     "matvec": ("q4_matvec.hip", "q4_device.h"),
     "lmhead": ("q4_matvec.hip", "q4_device.h"),
     "matmul": ("q4_matmul.hip", "q4_smallm.hip", "q4_device.h"),
+    "encoder": ("q4_matmul.hip", "q4_smallm.hip", "q4_device.h"),
+    "prefix": ("q4_matmul.hip", "q4_smallm.hip", "q4_device.h"),
+    "decode": ("q4_matvec.hip", "q4_device.h"),
     "embed": ("q4_embed_quant.hip", "q4_device.h"),
 }
 
@@ -87,6 +101,23 @@ def source_hash(workload: str) -> str:
             h.update(name.encode())
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def profile_call_us(path: str, workload: str):
+    """Kernel time per call of a workload from a trace summary in profiles/
+    (the sum of its library kernels' timed-window means), if the summary was
+    taken on the current sources of those kernels; else None."""
+    if not os.path.exists(path):
+        return None
+    total, found, hash_ok = 0.0, False, False
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source_hash:"):
+                hash_ok = line.split(":", 1)[1].strip() == source_hash(workload)
+            elif line.startswith("window_mean_us["):
+                total += float(line.split("]:", 1)[1].split()[0])
+                found = True
+    return total if (found and hash_ok) else None
 
 
 def dispatches_per_call(workload: str) -> int:
@@ -206,21 +237,23 @@ def _run(workload: str, iters: int, graph: bool = False) -> None:
     torch.cuda.synchronize()
     r = len(ws)
     if graph:
-        # the bench's timing mode: one HIP graph of r rotated calls on the
-        # launch stream, replayed; mean per call from HIP events on that
-        # stream over the timed replays
+        # the bench's timing mode (bench.py, timed()): one HIP graph of the r
+        # rotated calls repeated to at least 200 calls on the launch stream,
+        # max(2, 400 // n) untimed replays, then max(3, iters // n) timed
+        # ones; mean per call from HIP events on that stream
+        n = r * max(1, -(-200 // r))
         with torch.cuda.stream(s):
             for i in range(min(r, 3)):
                 call(i)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            for i in range(r):
+            for i in range(n):
                 call(i)
         torch.cuda.synchronize()
-        reps = max(1, -(-iters // r))
-        warm = max(2, 400 // r)
-        print(f"[profile] {workload}: graph of {r} calls, {warm} untimed + {reps} timed replays",
+        reps = max(3, iters // n)
+        warm = max(2, 400 // n)
+        print(f"[profile] {workload}: graph of {n} calls, {warm} untimed + {reps} timed replays",
               flush=True)
         with torch.cuda.stream(s):
             for _ in range(warm):
@@ -231,8 +264,8 @@ def _run(workload: str, iters: int, graph: bool = False) -> None:
                 g.replay()
             b.record(s)
         b.synchronize()
-        print(f"[profile] HIP events: {a.elapsed_time(b) * 1e3 / (reps * r):.3f} us per call "
-              f"over the {reps * r} timed calls", flush=True)
+        print(f"[profile] HIP events: {a.elapsed_time(b) * 1e3 / (reps * n):.3f} us per call "
+              f"over the {reps * n} timed calls (the last {reps * n} calls of the run)", flush=True)
         del g
     else:
         print(f"[profile] {workload}: {iters} calls", flush=True)
@@ -335,10 +368,18 @@ def _traffic(workload: str, fetch: str, write: str, out: str) -> None:
 
 # ----------------------------------------------------------------------------- counters
 
-def _counters(path: str, out: str | None) -> None:
+def _header(cmds) -> list:
+    """'# ' lines naming the commands that produced a summary."""
+    return [f"# {c}" for c in (cmds or [])]
+
+
+def _counters(path: str, out: str | None, cmds=None) -> None:
     """Per library kernel (and grid): mean of each counter per dispatch, and
-    the MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024
-    SIMDs) where both were collected (the figure rocprofv3 calls MfmaUtil)."""
+    the MFMA busy fraction where both counters were collected: busy cycles
+    summed over the 1024 SIMDs / (1024 x the kernel's GPU-active cycles).
+    rocprofv3 reports GRBM_GUI_ACTIVE summed over the chip's 8 XCDs (each
+    counts the same active cycles), so the active cycles are that sum / 8 --
+    the maximum over XCDs that rocprofv3's own MfmaUtil takes."""
     vals = defaultdict(lambda: defaultdict(list))
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
@@ -347,7 +388,7 @@ def _counters(path: str, out: str | None) -> None:
             grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
             vals[(_short(r["Kernel_Name"]), grid)][r["Counter_Name"]].append(float(r["Counter_Value"]))
     names = sorted({c for v in vals.values() for c in v})
-    lines = [f"{'kernel':44s} {'grid':>8s} {'n':>5s} " + " ".join(f"{c[:24]:>24s}" for c in names)
+    lines = _header(cmds) + [f"{'kernel':44s} {'grid':>8s} {'n':>5s} " + " ".join(f"{c[:24]:>24s}" for c in names)
              + ("  mfma_busy_%" if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(names) else "")]
     for (k, g), v in sorted(vals.items()):
         n = max(len(x) for x in v.values())
@@ -355,7 +396,8 @@ def _counters(path: str, out: str | None) -> None:
         line = f"{k[:44]:44s} {g:>8s} {n:5d} " + " ".join(f"{means.get(c, float('nan')):24.1f}"
                                                           for c in names)
         if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
-            line += f"  {100.0 * means['SQ_VALU_MFMA_BUSY_CYCLES'] / (means['GRBM_GUI_ACTIVE'] * 1024):11.1f}"
+            active = means["GRBM_GUI_ACTIVE"] / XCDS
+            line += f"  {100.0 * means['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * 1024):11.1f}"
         lines.append(line)
     text = "\n".join(lines) + "\n"
     if out:
@@ -371,9 +413,11 @@ def _short(name: str) -> str:
     return re.sub(r"\(.*", "", name).replace("void ", "")
 
 
-def _trace(path: str, out: str | None) -> None:
+def _trace(path: str, out: str | None, last: int = 0, workload: str | None = None,
+           cmds=None) -> None:
     rows = defaultdict(list)
     timeline = []
+    order = defaultdict(list)   # (kernel, grid) -> [(start, ns)] for the timed window
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
@@ -381,9 +425,10 @@ def _trace(path: str, out: str | None) -> None:
             grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
             wg = r.get("Workgroup_Size") or r.get("Workgroup_Size_X", "")
             rows[(_short(r["Kernel_Name"]), grid, wg)].append(ns)
+            order[(_short(r["Kernel_Name"]), grid)].append((t0, ns))
             if LIB_KERNEL in r["Kernel_Name"] and not any(k in r["Kernel_Name"] for k in SETUP_KERNELS):
                 timeline.append((t0, t1, _short(r["Kernel_Name"])))
-    lines = []
+    lines = _header(cmds)
     stats = path.replace("_kernel_trace.csv", "_kernel_stats.csv")
     if stats != path and os.path.exists(stats):  # rocprofv3 --stats of the same run
         lines.append("## rocprofv3 --stats (per kernel name)")
@@ -400,6 +445,19 @@ def _trace(path: str, out: str | None) -> None:
         v = sorted(v)
         lines.append(f"{k[:58]:58s} {g:>10s} {w:>4s} {len(v):7d} {sum(v) / len(v) / 1e3:9.3f} "
                      f"{v[len(v) // 2] / 1e3:9.3f} {v[0] / 1e3:8.3f}")
+    if last > 0:
+        # the timed window: the last `last` calls' dispatches of each library kernel
+        lines.append(f"## timed window: mean over the last dispatches of each library kernel "
+                     f"({last} calls)")
+        if workload:
+            lines.append(f"source_hash: {source_hash(workload)}")
+        lib_names = {t[2] for t in timeline}
+        for (k, g), v in sorted(order.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+            if k not in lib_names:
+                continue
+            v = [ns for _, ns in sorted(v)][-last:]
+            lines.append(f"window_mean_us[{k} grid={g}]: {sum(v) / len(v) / 1e3:.3f}  "
+                         f"(n={len(v)})")
     if len(timeline) > 1:
         # idle time between one library kernel's end and the next one's start
         timeline.sort()
@@ -436,18 +494,24 @@ def main(argv=None):
     s = sub.add_parser("trace")
     s.add_argument("csv")
     s.add_argument("--out")
+    s.add_argument("--last", type=int, default=0,
+                   help="also report each library kernel's mean over its last N dispatches")
+    s.add_argument("--workload", help="tag the summary with this workload's source hash")
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--out")
+    for q in (s, c):
+        q.add_argument("--cmd", action="append", dest="cmds",
+                       help="a command that produced the CSV, written as a '# ' header line")
     a = p.parse_args(argv)
     if a.cmd == "run":
         _run(a.workload, a.iters, a.graph)
     elif a.cmd == "traffic":
         _traffic(a.workload, a.fetch, a.write, a.out)
     elif a.cmd == "counters":
-        _counters(a.csv, a.out)
+        _counters(a.csv, a.out, a.cmds)
     else:
-        _trace(a.csv, a.out)
+        _trace(a.csv, a.out, a.last, a.workload, a.cmds)
 
 
 if __name__ == "__main__":

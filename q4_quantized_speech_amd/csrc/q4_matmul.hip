@@ -779,26 +779,49 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
   }
 }
 
-// Y = sum over s of P[s] in the order s = 0, 1, ... (deterministic).
+// Y = sum over s of P[s] in the order s = 0, 1, ... (deterministic).  A
+// thread requests all S of its slices before the first add: the slices were
+// just written by workgroups on every XCD, so each read goes out to memory,
+// and a chain of dependent load-then-add steps would pay that latency once
+// per slice (measured ~4 us per call on the prefix shapes, mostly waiting).
+template <int S>
 __global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restrict__ P,
-                                                          float* __restrict__ Y, int64_t mn,
-                                                          int splits) {
+                                                          float* __restrict__ Y, int64_t mn) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   if ((mn & 3) == 0) {
     const int64_t n4 = mn >> 2;
     const f32x4* p4 = reinterpret_cast<const f32x4*>(P);
     f32x4* y4 = reinterpret_cast<f32x4*>(Y);
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
-      f32x4 a = p4[i];
-      for (int s = 1; s < splits; ++s) a += p4[i + s * n4];
+      f32x4 v[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) v[s] = p4[i + s * n4];
+      f32x4 a = v[0];
+#pragma unroll
+      for (int s = 1; s < S; ++s) a += v[s];
       y4[i] = a;
     }
   } else {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < mn; i += stride) {
-      float a = P[i];
-      for (int s = 1; s < splits; ++s) a += P[i + s * mn];
+      float v[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) v[s] = P[i + s * mn];
+      float a = v[0];
+#pragma unroll
+      for (int s = 1; s < S; ++s) a += v[s];
       Y[i] = a;
     }
+  }
+}
+
+template <int S>
+void launch_fold(const float* P, float* y, int64_t mn, int splits, int blocks, hipStream_t s) {
+  if constexpr (S <= MAX_SPLITS) {
+    if (splits == S) {
+      hipLaunchKernelGGL(splitk_fold_kernel<S>, dim3(blocks), dim3(256), 0, s, P, y, mn);
+      return;
+    }
+    launch_fold<S + 1>(P, y, mn, splits, blocks, s);
   }
 }
 
@@ -1053,6 +1076,7 @@ static void launch_skinny(const uint8_t* w, const float* x, float* y, float* P, 
 hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                          int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
   const MatmulPlan p = plan_matmul(M, N, K, cus, ws ? ws_bytes : 0);
+  if (p.splits > MAX_SPLITS) return hipErrorInvalidValue;  // the planner caps it; the fold relies on it
   float* P = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
   switch (p.kind) {
     case MM_STREAM:
@@ -1101,7 +1125,7 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
     const int64_t mn = M * N;
     const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
     const int blocks = static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
-    hipLaunchKernelGGL(splitk_fold_kernel, dim3(blocks), dim3(256), 0, s, P, y, mn, p.splits);
+    launch_fold<2>(P, y, mn, p.splits, blocks, s);
   }
   return hipGetLastError();
 }

@@ -323,6 +323,31 @@ def split_canary_workspace(m, n, k, sentinel):
     return ws, need
 
 
+def test_matmul_every_split_count():
+    """The fold is compiled once per K-split count (2 to 16): a workspace of
+    s partial slices caps the split at s, so every count is reached, on the
+    wide kernel (K = 12288 in 192 stages) and the skinny one; each result is
+    held to the oracle's binary16 bound and repeats bit for bit."""
+    reached = set()
+    for (m, n, k) in [(96, 512, 12288), (8, 130, 12288)]:
+        qb_h = O.quantize_q4_0(_rand_w(n, k, 31))
+        x_h = _rand_x(m, k, 32)
+        ref, b = O.matmul_f64(qb_h, x_h, n, k)
+        qb, x = dev(qb_h), dev(x_h)
+        for s in range(2, 17):
+            nbytes = s * m * n * 4
+            route, splits = q4.matmul_route(m, n, k, nbytes)
+            assert 2 <= splits <= s, (route, splits, s)
+            reached.add(splits)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            announce(f"matmul split count {route} {splits} (cap {s}) {m}x{n}x{k}")
+            y1 = host(q4.matmul(qb, x, workspace=ws))
+            y2 = host(q4.matmul(qb, x, workspace=ws))
+            assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+            assert_within(y1, ref, b, O.MFMA_REL, O.MFMA_ABS, f"{route} splits={splits} {m}x{n}x{k}")
+    assert reached == set(range(2, 17)), sorted(reached)
+
+
 @pytest.mark.parametrize("m,n,k", [(70, 150, 2048), (300, 256, 1024), (375, 1280, 1280),
                                    (1500, 1280, 5120), (40, 3072, 9216)])
 def test_matmul_split_k_stays_in_bounds(m, n, k):

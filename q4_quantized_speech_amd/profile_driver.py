@@ -63,6 +63,7 @@ CACHE_DEFEAT_BYTES = 1 << 30
 XCDS = 8                       # accelerator complex dies of the MI355X (GRBM counter instances)
 CAL_BYTES = 256 << 20          # calibration kernel: reads and writes this many bytes
 CAL_KERNEL = "neg_kernel"      # substring of torch's element-wise negation kernel
+MARKER_KERNEL = "bitwise_not"  # launched right before the timed replays of ``run --graph``
 LIB_KERNEL = "q4::"            # namespace of the library's kernels
 SETUP_KERNELS = ("quantize_kernel",)  # library kernels that only prepare inputs
 
@@ -109,7 +110,7 @@ def profile_call_us(path: str, workload: str):
     taken on the current sources of those kernels; else None."""
     if not os.path.exists(path):
         return None
-    total, found, hash_ok = 0.0, False, False
+    total, found, hash_ok, per_call = 0.0, False, False, None
     with open(path) as fh:
         for line in fh:
             if line.startswith("source_hash:"):
@@ -117,7 +118,13 @@ def profile_call_us(path: str, workload: str):
             elif line.startswith("window_mean_us["):
                 total += float(line.split("]:", 1)[1].split()[0])
                 found = True
-    return total if (found and hash_ok) else None
+            elif line.startswith("call_kernel_us:"):
+                per_call = float(line.split(":", 1)[1].split()[0])
+    if not hash_ok:
+        return None
+    if per_call is not None:
+        return per_call
+    return total if found else None
 
 
 def dispatches_per_call(workload: str) -> int:
@@ -255,9 +262,13 @@ def _run(workload: str, iters: int, graph: bool = False) -> None:
         warm = max(2, 400 // n)
         print(f"[profile] {workload}: graph of {n} calls, {warm} untimed + {reps} timed replays",
               flush=True)
+        marker = torch.zeros(1, dtype=torch.int32, device=dev)
         with torch.cuda.stream(s):
             for _ in range(warm):
                 g.replay()
+            # a kernel no other step launches: the trace's timed window
+            # begins at its dispatch
+            torch.bitwise_not(marker, out=marker)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(s)
             for _ in range(reps):
@@ -417,6 +428,7 @@ def _trace(path: str, out: str | None, last: int = 0, workload: str | None = Non
            cmds=None) -> None:
     rows = defaultdict(list)
     timeline = []
+    markers = []                # start times of the marker kernel
     order = defaultdict(list)   # (kernel, grid) -> [(start, ns)] for the timed window
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
@@ -425,6 +437,8 @@ def _trace(path: str, out: str | None, last: int = 0, workload: str | None = Non
             grid = r.get("Grid_Size") or r.get("Grid_Size_X", "")
             wg = r.get("Workgroup_Size") or r.get("Workgroup_Size_X", "")
             rows[(_short(r["Kernel_Name"]), grid, wg)].append(ns)
+            if MARKER_KERNEL in r["Kernel_Name"]:
+                markers.append(t0)
             order[(_short(r["Kernel_Name"]), grid)].append((t0, ns))
             if LIB_KERNEL in r["Kernel_Name"] and not any(k in r["Kernel_Name"] for k in SETUP_KERNELS):
                 timeline.append((t0, t1, _short(r["Kernel_Name"])))
@@ -446,18 +460,39 @@ def _trace(path: str, out: str | None, last: int = 0, workload: str | None = Non
         lines.append(f"{k[:58]:58s} {g:>10s} {w:>4s} {len(v):7d} {sum(v) / len(v) / 1e3:9.3f} "
                      f"{v[len(v) // 2] / 1e3:9.3f} {v[0] / 1e3:8.3f}")
     if last > 0:
-        # the timed window: the last `last` calls' dispatches of each library kernel
-        lines.append(f"## timed window: mean over the last dispatches of each library kernel "
-                     f"({last} calls)")
-        if workload:
-            lines.append(f"source_hash: {source_hash(workload)}")
         lib_names = {t[2] for t in timeline}
-        for (k, g), v in sorted(order.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
-            if k not in lib_names:
-                continue
-            v = [ns for _, ns in sorted(v)][-last:]
-            lines.append(f"window_mean_us[{k} grid={g}]: {sum(v) / len(v) / 1e3:.3f}  "
-                         f"(n={len(v)})")
+        if markers:
+            # the timed window: every library dispatch after the last marker
+            t0 = max(markers)
+            lines.append(f"## timed window: library dispatches after the marker kernel "
+                         f"({last} calls)")
+            if workload:
+                lines.append(f"source_hash: {source_hash(workload)}")
+            total = 0
+            for (k, g), v in sorted(order.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+                if k not in lib_names:
+                    continue
+                v = [ns for st, ns in v if st > t0]
+                if not v:
+                    continue
+                total += sum(v)
+                lines.append(f"window_mean_us[{k} grid={g}]: {sum(v) / len(v) / 1e3:.3f}  "
+                             f"(n={len(v)}, {len(v) / last:g} per call)")
+            lines.append(f"call_kernel_us: {total / last / 1e3:.3f}  (sum of the window's "
+                         f"library kernel time / {last} calls)")
+        else:
+            # no marker (older runs): the last `last` dispatches of each
+            # (kernel, grid); kernels sharing a grid are then counted once
+            lines.append(f"## timed window: mean over the last dispatches of each library kernel "
+                         f"({last} calls)")
+            if workload:
+                lines.append(f"source_hash: {source_hash(workload)}")
+            for (k, g), v in sorted(order.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+                if k not in lib_names:
+                    continue
+                v = [ns for _, ns in sorted(v)][-last:]
+                lines.append(f"window_mean_us[{k} grid={g}]: {sum(v) / len(v) / 1e3:.3f}  "
+                             f"(n={len(v)})")
     if len(timeline) > 1:
         # idle time between one library kernel's end and the next one's start
         timeline.sort()

@@ -86,10 +86,13 @@ size_t q4_row_bytes(int64_t K);
  * within 1e-4 * sum_k |w_k x_k| + 1e-6 for any finite x whose per-block sums
  * sum_j |q_j - 8| |x_j| stay below the float32 maximum (|x| < 1.3e36
  * always does; a zero weight, q = 8, adds exactly nothing whatever its x),
- * and results that fit in float32.  Tuned for M = 1; each row of x runs its own workgroups,
- * which re-read W (mostly from the caches when W is small).  Results are
- * deterministic (fixed reduction order) and a row's result does not depend
- * on the other rows of x.
+ * and results that fit in float32.  Tuned for M = 1.  With M >= 2 the rows of
+ * x are taken in pairs: each pair's workgroups read and decode W once and
+ * multiply it into both rows (K % 64 == 0, K <= 12288; otherwise each row
+ * runs its own workgroups), so W is read ceil(M / 2) times (mostly from the
+ * caches when W is small).  Results are deterministic (fixed reduction
+ * order) and a row's result does not depend on the other rows of x: every
+ * row has the bits it has in a call with that row alone.
  */
 q4_status q4_matvec(const void* w_q4, const float* x, float* y,
                     int64_t M, int64_t N, int64_t K, void* stream);
@@ -115,10 +118,10 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  * scale exceeds 8188 in magnitude (largest |w| above 65504, which an encoder
  * only writes for weights that large) decodes to +-inf on this path.  M <= 4
  * (several decode streams) meets the q4_matvec bound, over q4_matvec's range
- * of x: either each row of x goes through the q4_matvec
- * kernel (one row, K % 64 == 32, and weights small enough that the rows'
- * repeated reads stay in the caches: (M - 1) * N * K * 18/32 bytes up to
- * 40 MiB, K <= 12288), or the weights are read once and enter the matrix
+ * of x: either the rows of x go through the q4_matvec
+ * kernel (one or two rows, K % 64 == 32, and weights small enough that the
+ * rows' repeated reads stay in the caches: (M - 1) * N * K * 18/32 bytes up
+ * to 40 MiB, K <= 12288), or the weights are read once and enter the matrix
  * cores exactly (q - 8, block scale applied in float32) with x as two
  * binary16 parts after a power-of-two scaling per 256-value chunk of a row;
  * a chunk whose nonzero magnitudes span more than 2^20 (or reach 2^124) is
@@ -236,8 +239,8 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  * kernel; a caller may log them).  Both return a static string, or NULL for
  * a shape the entry point rejects; they enqueue nothing.
  * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
- *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel per
- *   row of x), "small" (M <= 4, weights read once), "skinny" (prompt
+ *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
+ *   rows of x in pairs), "small" (M <= 4, weights read once), "skinny" (prompt
  *   prefixes), "wide128" / "wide64" (tiles of 128 or 64 rows of X by 256
  *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
  *   -- and, if splits is not NULL, its number of K splits (1: none).

@@ -937,11 +937,11 @@ struct MatmulPlan {
 };
 
 // Up to 4 rows of x (decode streams) keep the float32 accuracy of q4_matvec.
-// The matvec kernel, one set of workgroups per row of x, serves one row, any
-// K % 64 == 32 and the shapes whose repeated weight reads stay in the caches
-// ((M - 1) * weight bytes up to STREAM_REREAD: measured faster there, it has
-// no split and no fold launch); the small-M MFMA kernel, weights read once,
-// the rest.  Skinny for prompt-prefix row counts (bound by streaming W);
+// The matvec kernel (one set of workgroups per pair of rows of x, each
+// weight read once per pair) serves one or two rows, any K % 64 == 32 and
+// the shapes whose repeated weight reads stay in the caches ((M - 1) *
+// weight bytes up to STREAM_REREAD: measured faster there, it has no split
+// and no fold launch); the small-M MFMA kernel, weights read once, the rest.  Skinny for prompt-prefix row counts (bound by streaming W);
 // 128 x 256 wave-specialised tiles for wide outputs (half the X traffic per
 // flop of 128 x 128); 128 x 128 tiles otherwise.  K is split when the units
 // alone cannot fill every workgroup slot: at least `min_st` stages per split,
@@ -951,7 +951,7 @@ constexpr int64_t STREAM_REREAD = int64_t{40} << 20;
 static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   if (M <= 4) {
     const int64_t wbytes = N * (K / 32) * 18;
-    if (M == 1 || K % 64 != 0 || (K <= 12288 && (M - 1) * wbytes <= STREAM_REREAD))
+    if (M == 1 || K % 64 != 0 || (K <= 12288 && (M == 2 || (M - 1) * wbytes <= STREAM_REREAD)))
       return MatmulPlan{MM_STREAM, 1, 0};
   }
   if (K % 64 != 0) return MatmulPlan{MM_SIMPLE, 1, 0};

@@ -62,10 +62,13 @@ namespace {
 // a v_fma_mix right after the one it depends on costs a wait state.
 // `magic` is 0x64006400 held in a VGPR (the caller keeps it there), so each
 // mask-and-insert is one v_and_or_b32 (a VOP3 takes at most one scalar
-// constant).
-__device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, f32x4 xl0, f32x4 xh0, float& acc0,
-                                              uint32_t q1, f32x4 xl1, f32x4 xh1, float& acc1,
-                                              uint32_t magic) {
+// constant).  With MX rows of x the codes are decoded once and multiplied
+// into each row's own pair of chains.
+template <int MX>
+__device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, uint32_t q1, const f32x4 (&xl0)[MX],
+                                              const f32x4 (&xh0)[MX], const f32x4 (&xl1)[MX],
+                                              const f32x4 (&xh1)[MX], float (&acc0)[MX],
+                                              float (&acc1)[MX], uint32_t magic) {
   const f16x2 lo_off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
   const f16x2 hi_off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
   const uint32_t v0 = q0 >> 8, v1 = q1 >> 8;
@@ -77,25 +80,29 @@ __device__ __forceinline__ void nib_dot8_mix2(uint32_t q0, f32x4 xl0, f32x4 xh0,
   const f16x2 c1 = __builtin_bit_cast(f16x2, (v1 & 0x000F000Fu) | magic) + lo_off;
   const f16x2 e0 = __builtin_bit_cast(f16x2, (v0 & 0x00F000F0u) | magic) + hi_off;
   const f16x2 e1 = __builtin_bit_cast(f16x2, (v1 & 0x00F000F0u) | magic) + hi_off;
-  float s0 = acc0, s1 = acc1;
-  s0 = __builtin_fmaf(static_cast<float>(a0.x), xl0.x, s0);
-  s1 = __builtin_fmaf(static_cast<float>(a1.x), xl1.x, s1);
-  s0 = __builtin_fmaf(static_cast<float>(c0.x), xl0.y, s0);
-  s1 = __builtin_fmaf(static_cast<float>(c1.x), xl1.y, s1);
-  s0 = __builtin_fmaf(static_cast<float>(a0.y), xl0.z, s0);
-  s1 = __builtin_fmaf(static_cast<float>(a1.y), xl1.z, s1);
-  s0 = __builtin_fmaf(static_cast<float>(c0.y), xl0.w, s0);
-  s1 = __builtin_fmaf(static_cast<float>(c1.y), xl1.w, s1);
-  s0 = __builtin_fmaf(static_cast<float>(b0.x), xh0.x, s0);
-  s1 = __builtin_fmaf(static_cast<float>(b1.x), xh1.x, s1);
-  s0 = __builtin_fmaf(static_cast<float>(e0.x), xh0.y, s0);
-  s1 = __builtin_fmaf(static_cast<float>(e1.x), xh1.y, s1);
-  s0 = __builtin_fmaf(static_cast<float>(b0.y), xh0.z, s0);
-  s1 = __builtin_fmaf(static_cast<float>(b1.y), xh1.z, s1);
-  s0 = __builtin_fmaf(static_cast<float>(e0.y), xh0.w, s0);
-  s1 = __builtin_fmaf(static_cast<float>(e1.y), xh1.w, s1);
-  acc0 = s0;
-  acc1 = s1;
+  // each row of x: its own two chains, in the same order whatever MX
+#pragma unroll
+  for (int i = 0; i < MX; ++i) {
+    float s0 = acc0[i], s1 = acc1[i];
+    s0 = __builtin_fmaf(static_cast<float>(a0.x), xl0[i].x, s0);
+    s1 = __builtin_fmaf(static_cast<float>(a1.x), xl1[i].x, s1);
+    s0 = __builtin_fmaf(static_cast<float>(c0.x), xl0[i].y, s0);
+    s1 = __builtin_fmaf(static_cast<float>(c1.x), xl1[i].y, s1);
+    s0 = __builtin_fmaf(static_cast<float>(a0.y), xl0[i].z, s0);
+    s1 = __builtin_fmaf(static_cast<float>(a1.y), xl1[i].z, s1);
+    s0 = __builtin_fmaf(static_cast<float>(c0.y), xl0[i].w, s0);
+    s1 = __builtin_fmaf(static_cast<float>(c1.y), xl1[i].w, s1);
+    s0 = __builtin_fmaf(static_cast<float>(b0.x), xh0[i].x, s0);
+    s1 = __builtin_fmaf(static_cast<float>(b1.x), xh1[i].x, s1);
+    s0 = __builtin_fmaf(static_cast<float>(e0.x), xh0[i].y, s0);
+    s1 = __builtin_fmaf(static_cast<float>(e1.x), xh1[i].y, s1);
+    s0 = __builtin_fmaf(static_cast<float>(b0.y), xh0[i].z, s0);
+    s1 = __builtin_fmaf(static_cast<float>(b1.y), xh1[i].z, s1);
+    s0 = __builtin_fmaf(static_cast<float>(e0.y), xh0[i].w, s0);
+    s1 = __builtin_fmaf(static_cast<float>(e1.y), xh1[i].w, s1);
+    acc0[i] = s0;
+    acc1[i] = s1;
+  }
 }
 
 // Argmax bookkeeping: idx < 0 means "no candidate", which never wins over a
@@ -240,14 +247,22 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
 // SIMD) instead of living in 64 registers per lane (4 waves per SIMD).
 // G row groups of KS waves share the workgroup's x (each group stages a
 // quarter of it when G = 4) and cover 4 R G consecutive rows per pass.
-template <int KS, bool ARGMAX, int R, bool XL, int G>
+// MX rows of x per workgroup (1, or 2 for plain products): the weights are
+// read and decoded once for both rows; each row keeps its own chains in the
+// one-row order, so its results have the bits it would have alone.  A
+// missing second row (odd M) repeats the first and is never stored.
+template <int KS, bool ARGMAX, int R, bool XL, int G, int MX>
 __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
-    int K) {
+    int K, int M) {
+  static_assert(MX == 1 || (MX == 2 && !ARGMAX), "two rows of x only for plain products");
   constexpr int ROWS = 4 * R * G;  // rows per pass
-  __shared__ float red[2][KS][ROWS];
-  const int m = blockIdx.y;
+  __shared__ float red[2][KS][MX * ROWS];
+  const int m = blockIdx.y * MX;  // first row of x
+  int mr[MX];                     // the rows of x this workgroup reads
+#pragma unroll
+  for (int i = 0; i < MX; ++i) mr[i] = m + i < M ? m + i : m;
   const int nbp = K >> 6;
   const int64_t rb = static_cast<int64_t>(nbp) * PAIR_BYTES;
   const int tid = threadIdx.x;
@@ -287,51 +302,60 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
   // wait for the weights; x goes to LDS (kept there, or copied to this lane's
   // registers), in rows of 64 floats padded to 68 so the 16 lanes of a DPP
   // row hit distinct banks.
-  __shared__ float xs[KS][16][68];
-  f32x4 xg[4];
-  {
-    const float* xw = X + static_cast<int64_t>(m) * K + 1024 * ks;
+  __shared__ float xs[MX][KS][16][68];
+  f32x4 xg[MX][4];
+#pragma unroll
+  for (int i = 0; i < MX; ++i) {
+    const float* xw = X + static_cast<int64_t>(mr[i]) * K + 1024 * ks;
     const int lim = K - 1024 * ks;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = (u * 64 + (tid & 63)) * 4;
       if (u % G == gi)
-        xg[u] = p < lim ? *reinterpret_cast<const f32x4*>(xw + p) : f32x4{0.f, 0.f, 0.f, 0.f};
+        xg[i][u] = p < lim ? *reinterpret_cast<const f32x4*>(xw + p) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   load(row0, wa);
   load(row0 + stride, wb);
   // x of the high nibbles is divided by 16 (exact) on the way in
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (u % G != gi) continue;
-    const int p = u * 64 + (tid & 63);
-    f32x4 v = xg[u];
-    if (p & 4) v *= 0.0625f;
-    *reinterpret_cast<f32x4*>(&xs[ks][p >> 4][(p & 15) * 4]) = v;
-  }
-  __syncthreads();
-  const float* xr = &xs[ks][j][0];
-  float xv[XL ? 1 : 64];
-  if constexpr (!XL) {
+  for (int i = 0; i < MX; ++i) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * t);
-      xv[4 * t] = v.x; xv[4 * t + 1] = v.y; xv[4 * t + 2] = v.z; xv[4 * t + 3] = v.w;
+    for (int u = 0; u < 4; ++u) {
+      if (u % G != gi) continue;
+      const int p = u * 64 + (tid & 63);
+      f32x4 v = xg[i][u];
+      if (p & 4) v *= 0.0625f;
+      *reinterpret_cast<f32x4*>(&xs[i][ks][p >> 4][(p & 15) * 4]) = v;
     }
   }
-  // the 16 x values of step t: low and high nibbles of the two blocks
-  auto xstep = [&](int t, int xo, f32x4& xl0, f32x4& xh0, f32x4& xl1, f32x4& xh1) {
+  __syncthreads();
+  float xv[MX][XL ? 1 : 64];
+  if constexpr (!XL) {
+#pragma unroll
+    for (int i = 0; i < MX; ++i) {
+      const float* xr = &xs[i][ks][j][0];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * t);
+        xv[i][4 * t] = v.x; xv[i][4 * t + 1] = v.y; xv[i][4 * t + 2] = v.z; xv[i][4 * t + 3] = v.w;
+      }
+    }
+  }
+  // the 16 x values of step t for row i: low and high nibbles of the two blocks
+  auto xstep = [&](int i, int t, int xo, f32x4& xl0, f32x4& xh0, f32x4& xl1, f32x4& xh1) {
     if constexpr (XL) {
+      const float* xr = &xs[i][ks][j][0];
       xl0 = *reinterpret_cast<const f32x4*>(xr + xo + 4 * t);
       xh0 = *reinterpret_cast<const f32x4*>(xr + xo + 16 + 4 * t);
       xl1 = *reinterpret_cast<const f32x4*>(xr + xo + 32 + 4 * t);
       xh1 = *reinterpret_cast<const f32x4*>(xr + xo + 48 + 4 * t);
     } else {
-      xl0 = f32x4{xv[4 * t], xv[4 * t + 1], xv[4 * t + 2], xv[4 * t + 3]};
-      xh0 = f32x4{xv[16 + 4 * t], xv[17 + 4 * t], xv[18 + 4 * t], xv[19 + 4 * t]};
-      xl1 = f32x4{xv[32 + 4 * t], xv[33 + 4 * t], xv[34 + 4 * t], xv[35 + 4 * t]};
-      xh1 = f32x4{xv[48 + 4 * t], xv[49 + 4 * t], xv[50 + 4 * t], xv[51 + 4 * t]};
+      const float* v = xv[i];
+      xl0 = f32x4{v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
+      xh0 = f32x4{v[16 + 4 * t], v[17 + 4 * t], v[18 + 4 * t], v[19 + 4 * t]};
+      xl1 = f32x4{v[32 + 4 * t], v[33 + 4 * t], v[34 + 4 * t], v[35 + 4 * t]};
+      xh1 = f32x4{v[48 + 4 * t], v[49 + 4 * t], v[50 + 4 * t], v[51 + 4 * t]};
     }
   };
 
@@ -340,21 +364,25 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
   const uint32_t dmask = cvalid ? 0xFFFFu : 0u;
   uint32_t magic = 0x64006400u;  // binary16 1024 in both halves
   asm("" : "+v"(magic));
-  // sum over this lane's pair for R rows: d0 * sum (q - 8) x + d1 * (...)
-  auto compute = [&](uint32_t (&w)[R][9], float (&acc)[R]) {
+  // sum over this lane's pair for R rows of W and MX rows of x:
+  // d0 * sum (q - 8) x + d1 * (...)
+  auto compute = [&](uint32_t (&w)[R][9], float (&acc)[MX][R]) {
     int xo = 0;  // opaque per pass, so the LDS reads of x stay in the pass
     if constexpr (XL) asm volatile("" : "+v"(xo));
-    float s0[R], s1[R];
+    float s0[R][MX], s1[R][MX];
 #pragma unroll
-    for (int r = 0; r < R; ++r) s0[r] = s1[r] = 0.f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < MX; ++i) s0[r][i] = s1[r][i] = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      f32x4 xl0, xh0, xl1, xh1;
-      xstep(t, xo, xl0, xh0, xl1, xh1);
+      f32x4 xl0[MX], xh0[MX], xl1[MX], xh1[MX];
+#pragma unroll
+      for (int i = 0; i < MX; ++i) xstep(i, t, xo, xl0[i], xh0[i], xl1[i], xh1[i]);
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        nib_dot8_mix2(shift16(w[r][t + 1], w[r][t]), xl0, xh0, s0[r], w[r][5 + t], xl1, xh1,
-                      s1[r], magic);
+        nib_dot8_mix2<MX>(shift16(w[r][t + 1], w[r][t]), w[r][5 + t], xl0, xh0, xl1, xh1, s0[r],
+                          s1[r], magic);
       // one step's x live at a time
       if constexpr (XL) __builtin_amdgcn_sched_barrier(0);
     }
@@ -362,7 +390,8 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     for (int r = 0; r < R; ++r) {
       const float d0 = half_bits_to_float(w[r][0] & dmask);
       const float d1 = half_bits_to_float((w[r][4] >> 16) & dmask);
-      acc[r] = __builtin_fmaf(d1, s1[r], d0 * s0[r]);
+#pragma unroll
+      for (int i = 0; i < MX; ++i) acc[i][r] = __builtin_fmaf(d1, s1[r][i], d0 * s0[r][i]);
     }
   };
 
@@ -374,39 +403,50 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
   // a store through a resource covering this pass's rows of Y, with an
   // out-of-range offset for all lanes but one per row, or the argmax update
   // as selects.
-  auto finish = [&](int64_t r0, float (&acc)[R], int q) {
+  auto finish = [&](int64_t r0, float (&acc)[MX][R], int q) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = row16_sum(acc[r]);
+    for (int i = 0; i < MX; ++i)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[i][r] = row16_sum(acc[i][r]);
     if constexpr (KS > 1) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) red[q][ks][grp * R + r] = acc[r];
+      for (int i = 0; i < MX; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[q][ks][i * ROWS + grp * R + r] = acc[i][r];
       __syncthreads();
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float sum = red[q][0][grp * R + r];
-        for (int u = 1; u < KS; ++u) sum += red[q][u][grp * R + r];
-        acc[r] = sum;
+      for (int i = 0; i < MX; ++i) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float sum = red[q][0][i * ROWS + grp * R + r];
+          for (int u = 1; u < KS; ++u) sum += red[q][u][i * ROWS + grp * R + r];
+          acc[i][r] = sum;
+        }
       }
     }
     if constexpr (ARGMAX) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = static_cast<int>(r0) + grp * R + r;
-        const bool take = ks == 0 && row < N && am_better(acc[r], row, bv, bi);
-        bv = take ? acc[r] : bv;
+        const bool take = ks == 0 && row < N && am_better(acc[0][r], row, bv, bi);
+        bv = take ? acc[0][r] : bv;
         bi = take ? row : bi;
       }
     } else {
       const int64_t left = N - r0;  // >= 1
-      const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
-          Y + static_cast<int64_t>(m) * N + r0, 0, static_cast<int>((left < ROWS ? left : ROWS) * 4),
-          0x00020000);
       const bool writer = ks == 0 && j == 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float val = acc[r];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ys,
-                                              writer ? (grp * R + r) * 4 : 0x40000000, 0, 0);
+      for (int i = 0; i < MX; ++i) {
+        if (i > 0 && m + i >= M) continue;  // the missing second row (uniform)
+        const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+            Y + static_cast<int64_t>(m + i) * N + r0, 0,
+            static_cast<int>((left < ROWS ? left : ROWS) * 4), 0x00020000);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float val = acc[i][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ys,
+                                                writer ? (grp * R + r) * 4 : 0x40000000, 0, 0);
+        }
       }
     }
   };
@@ -414,14 +454,14 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
   // ping-pong over passes, two in flight; passes past the end read as zeros
   // (no traffic)
   for (;;) {
-    float acc[R];
+    float acc[MX][R];
     compute(wa, acc);
     finish(row0, acc, 0);
     const int64_t r1 = row0 + stride;
     if (r1 >= N) break;
     load(r1 + stride, wa);
     __builtin_amdgcn_sched_barrier(0);
-    float acc2[R];
+    float acc2[MX][R];
     compute(wb, acc2);
     finish(r1, acc2, 1);
     row0 = r1 + stride;
@@ -483,12 +523,12 @@ struct PairGrid {
   int64_t g;         // workgroups
   int64_t cu_rows;   // rows handled by the busiest CU
 };
-template <int KS, bool ARGMAX, int R, bool XL, int G>
+template <int KS, bool ARGMAX, int R, bool XL, int G, int MX = 1>
 PairGrid pair_grid(int64_t N) {
   static int per_cu = 0;  // per process; the kernel's resource use is fixed
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL, G>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL, G, MX>,
                                                       64 * KS * G, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -524,13 +564,28 @@ PairVariant pair_variant(int64_t N) {
   return one ? PV_REG_R1 : PV_REG_R2;
 }
 
+// Plain products with two or more rows of x take two rows per workgroup
+// (the weights are read and decoded once per pair of rows) and, with x in
+// registers, one weight row per lane (two rows of x at R = 2 would spill);
+// the argmax takes one row of x per workgroup.
 template <int KS, bool ARGMAX, int R, bool XL, int G>
 void launch_variant(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const PairGrid g = pair_grid<KS, ARGMAX, R, XL, G>(N);
-  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, R, XL, G>),
+  if constexpr (!ARGMAX) {
+    if (M >= 2) {
+      constexpr int R2 = XL ? R : 1;
+      const PairGrid g = pair_grid<KS, ARGMAX, R2, XL, G, 2>(N);
+      hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, R2, XL, G, 2>),
+                         dim3(static_cast<unsigned>(g.g), static_cast<unsigned>((M + 1) / 2)),
+                         dim3(64 * KS * G), 0, s, w, x, y, idx, val, ws, N, static_cast<int>(K),
+                         static_cast<int>(M));
+      return;
+    }
+  }
+  const PairGrid g = pair_grid<KS, ARGMAX, R, XL, G, 1>(N);
+  hipLaunchKernelGGL((matvec_pairs_kernel<KS, ARGMAX, R, XL, G, 1>),
                      dim3(static_cast<unsigned>(g.g), M), dim3(64 * KS * G), 0, s, w, x, y, idx,
-                     val, ws, N, static_cast<int>(K));
+                     val, ws, N, static_cast<int>(K), static_cast<int>(M));
 }
 
 template <int KS, bool ARGMAX>

@@ -597,3 +597,23 @@ def test_no_write_past_outputs():
     buf = torch.full((3 * k + 64,), sentinel, dtype=torch.float32, device="cuda")
     q4.embed_rows(qb, ids, out=buf[: 3 * k].view(3, k))
     assert np.all(host(buf)[3 * k:] == sentinel)
+
+
+@pytest.mark.parametrize("n,k", [(300, 1088), (3000, 3072), (3072, 4096), (700, 9216),
+                                 (65600, 1024), (70, 12320), (40, 13312)])
+@pytest.mark.parametrize("m", [2, 3, 5, 8])
+def test_matvec_rows_as_alone(m, n, k):
+    """Rows of x taken in pairs by one workgroup (weights decoded once for
+    both) give every row the bits it has in a call with that row alone, on
+    every variant (x in LDS, four row groups, x in registers, the generic
+    kernel) and with an odd last row; each row also meets the oracle."""
+    qb = O.quantize_q4_0(_rand_w(n, k, 41 + m))
+    x = _rand_x(m, k, 42 + m)
+    wq, xd = dev(qb), dev(x)
+    announce(f"matvec rows as alone {q4.matvec_route(n, k)} M={m} {n}x{k}")
+    y = host(q4.matvec(wq, xd))
+    ref, b = O.matmul_f64(qb, x, n, k)
+    assert_within(y, ref, b, *MV, f"rows as alone M={m} {n}x{k}")
+    for i in range(m):
+        yi = host(q4.matvec(wq, xd[i:i + 1]))[0]
+        assert np.array_equal(y[i].view(np.uint32), yi.view(np.uint32)), (m, i)

@@ -1,7 +1,7 @@
 """q4_matmul with 1 to 4 rows of x meets the matvec bound (1e-4 * B + 1e-6),
-not only the binary16 one, on both of its routes: the matvec kernel once per
-row of x (one row, K % 64 == 32, weights whose repeated reads stay in the
-caches) and the small-M kernel (weights read once and multiplied on the matrix
+not only the binary16 one, on both of its routes: the matvec kernel (rows of
+x in pairs; one or two rows, K % 64 == 32, weights whose repeated reads stay
+in the caches) and the small-M kernel (weights read once and multiplied on the matrix
 cores with exact q - 8 operands, the block scales applied in float32 and x
 carried as two binary16 parts; K > 12288 always takes it).  Row counts just
 past it (5 to 16) take the binary16 kernels and are held to the binary16
@@ -133,10 +133,12 @@ def test_small_m_deterministic_and_in_bounds():
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 3072, 4096),
-                                   (3, 65, 1056), (2, 18432, 3072)])
+                                   (3, 65, 1056), (2, 18432, 3072), (2, 65536, 3072),
+                                   (2, 3072, 9216)])
 def test_small_m_stream_route_is_matvec(m, n, k):
     """Where the rows go through the matvec kernel, q4_matmul returns exactly
-    q4_matvec's bits (the same kernel, no workspace planned)."""
+    q4_matvec's bits (the same kernel, no workspace planned); two rows of x
+    take that route whatever the size of W (each pair reads W once)."""
     assert int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) == 0
     qb = dev(weights_q4(n, k, synth.seed_for(1, n + k)))
     x = dev(synth.activations(m, k, synth.seed_for(3, m + k)))

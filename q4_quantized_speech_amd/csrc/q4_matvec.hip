@@ -34,7 +34,10 @@
 //  * the 16 lanes of a row are summed in their DPP row, the KS waves' partial
 //    sums are then added in LDS in a fixed order (deterministic results);
 //  * workgroups are persistent (a grid-stride loop over row groups), as many
-//    as are resident at once, with the passes spread evenly over them.
+//    as are resident at once, with the passes spread evenly over them;
+//  * with two or more rows of x, a workgroup takes them in pairs: the codes
+//    are loaded and decoded once and feed each row's own chains, in the
+//    order of the one-row kernel (every row keeps the bits it has alone).
 // The argmax variant (the LM head over the 131072-row table that section
 // "Solutions techniques", item 3, keeps in Q4) tracks the best (value, lowest
 // index) per lane, reduces it per workgroup, and folds it into a per-row key

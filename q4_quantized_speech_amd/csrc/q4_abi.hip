@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/q4.h"
 #include "q4_kernels.h"
 
@@ -12,7 +14,9 @@ namespace q4 {
 namespace {
 thread_local int g_last_hip_error = 0;
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];  // 0 = not cached yet; benign race (idempotent)
+// 0 = not cached yet.  Threads that race on the first call all store the
+// same value; atomics keep that free of data races.
+std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,11 +38,11 @@ bool matmul_shape_ok(int64_t M, int64_t N, int64_t K) {
 DeviceInfo device_info() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DeviceInfo{256};
-  int cu = g_cu_count[dev];
+  int cu = g_cu_count[dev].load(std::memory_order_relaxed);
   if (cu == 0) {
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
       cu = 256;
-    g_cu_count[dev] = cu;
+    g_cu_count[dev].store(cu, std::memory_order_relaxed);
   }
   return DeviceInfo{cu};
 }

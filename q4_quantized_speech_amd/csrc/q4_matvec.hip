@@ -44,6 +44,7 @@
 // in the workspace with one device-scope atomic max; the last workgroup to
 // arrive writes the result and clears the workspace (no second launch).
 
+#include <atomic>
 #include <mutex>
 
 #include "q4_device.h"
@@ -528,13 +529,17 @@ struct PairGrid {
 };
 template <int KS, bool ARGMAX, int R, bool XL, int G, int MX = 1>
 PairGrid pair_grid(int64_t N) {
-  static int per_cu = 0;  // per process; the kernel's resource use is fixed
+  // per process (the kernel's resource use is fixed); racing first calls
+  // store the same value
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matvec_pairs_kernel<KS, ARGMAX, R, XL, G, MX>,
                                                       64 * KS * G, 0) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
+    per_cu_cache.store(nb, std::memory_order_relaxed);
   }
   const int64_t cus = device_info().cu_count;
   const int64_t passes = (N + 4 * R * G - 1) / (4 * R * G);

@@ -35,6 +35,8 @@
 //    weights are in flight.  K ranges of several workgroups (a K split) are
 //    added by the fold kernel in a fixed order: results are deterministic.
 
+#include <atomic>
+
 #include "q4_device.h"
 #include "q4_kernels.h"
 
@@ -363,12 +365,15 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 
 // Workgroups of the small-M kernel resident on one CU.
 int matmul_small_per_cu() {
-  static int per_cu = 0;  // per process; resource use is fixed
+  // per process (resource use is fixed); racing first calls store the same value
+  static std::atomic<int> cache{0};
+  int per_cu = cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &nb, matmul_small_kernel<SM_MAX_M>, SM_THREADS, 0);
     per_cu = (e == hipSuccess && nb > 0) ? nb : 1;
+    cache.store(per_cu, std::memory_order_relaxed);
   }
   return per_cu;
 }

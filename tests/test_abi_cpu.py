@@ -130,3 +130,42 @@ def test_header_is_plain_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "abi_smoke ok" in r.stdout, (r.stdout, r.stderr)
+
+
+# The routing decisions the kernels were measured for.  Without a GPU the
+# CU count falls back to 256 (the MI355X's) and the occupancy queries to one
+# workgroup per CU, so only the choices that do not depend on occupancy are
+# pinned here: the kernel family, and the wide kernel's tile height and split
+# (its cost model uses the CU count only).  The GPU tests assert the kernels
+# each route reaches.
+ROUTES = [
+    ((1, 18432, 3072), ("matvec", 1)),      # decode step
+    ((2, 18432, 3072), ("matvec", 1)),      # two streams: a pair of rows reads W once
+    ((2, 131072, 3072), ("matvec", 1)),     # at any size
+    ((4, 18432, 3072), ("small", None)),    # four streams, large W: weights read once
+    ((2, 64, 12352), ("small", None)),      # K > 12288: beyond the pair kernel
+    ((3, 300, 1056), ("matvec", 1)),        # K % 64 == 32 keeps the float32 path
+    ((16, 18432, 3072), ("skinny", None)),  # prompt prefix
+    ((76, 3072, 9216), ("skinny", None)),
+    ((200, 300, 1056), ("simple", 1)),      # K % 64 == 32, binary16 path
+    ((300, 256, 1024), ("tile", None)),     # narrow outputs
+    ((1500, 3840, 1280), ("wide128", 1)),   # encoder at M = 1500
+    ((1500, 1280, 1280), ("wide64", 1)),
+    ((1500, 5120, 1280), ("wide128", 1)),
+    ((1500, 1280, 5120), ("wide128", 4)),
+    ((375, 3072, 5120), ("wide128", 7)),    # adapter at M = 1500 / 4
+    ((375, 3840, 1280), ("wide64", 1)),     # encoder at M = 375
+    ((3000, 1280, 5120), ("wide128", 2)),
+]
+
+
+@pytest.mark.parametrize("shape,want", ROUTES)
+def test_matmul_routing(shape, want):
+    m, n, k = shape
+    need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k))
+    kind, splits = q4.matmul_route(m, n, k, need)
+    assert kind == want[0], (shape, kind, splits)
+    if want[1] is not None:
+        assert splits == want[1], (shape, kind, splits)
+    # a workspace of size 0 never splits
+    assert q4.matmul_route(m, n, k, 0)[1] == 1

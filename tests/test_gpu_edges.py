@@ -107,14 +107,16 @@ def test_subnormal_scales_argmax(n, k):
 
 # (M, N, K, workspace?): the kernel each lands on is asserted below
 MM_CASES = [
-    (2, 64, 3072, False),       # matvec kernel per row
+    (2, 64, 3072, False),       # matvec kernel (rows in pairs)
     (4, 64, 12352, True),       # small (weights read once), K split
     (4, 64, 12352, False),      # small, no split
     (40, 300, 2048, True),      # skinny
     (1500, 3840, 1280, True),   # wide128
-    (1500, 1280, 1280, True),   # wide64
+    (1500, 1280, 1280, True),   # wide32
     (1500, 1280, 5120, True),   # wide128 with a K split
-    (375, 1280, 1280, True),    # wide64 with a K split
+    (375, 1280, 1280, True),    # wide32 with a K split
+    (3000, 1280, 1280, True),   # wide64
+    (375, 1280, 5120, True),    # wide64 with a K split
     (300, 256, 1024, True),     # tile, K split
     (200, 300, 1056, False),    # simple (K % 64 == 32)
 ]
@@ -128,8 +130,8 @@ def test_matmul_kernels_are_all_covered():
         routes.add(r)
         if sp > 1:
             routes.add(r + "+split")
-    assert routes >= {"matvec", "small", "small+split", "skinny", "wide128", "wide64",
-                      "wide128+split", "wide64+split", "tile", "simple"}, routes
+    assert routes >= {"matvec", "small", "small+split", "skinny", "wide128", "wide64", "wide32",
+                      "wide128+split", "wide64+split", "wide32+split", "tile", "simple"}, routes
 
 
 def _one_hot_rows(m, k):

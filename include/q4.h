@@ -241,8 +241,8 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
  *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
  *   rows of x in pairs), "small" (M <= 4, weights read once), "skinny" (prompt
- *   prefixes), "wide128" / "wide64" / "wide32" (tiles of 128, 64 or 32 rows
- *   of X by 256 outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
+ *   prefixes), "wide128" / "wide96" / "wide64" / "wide32" (tiles of 128,
+ *   96, 64 or 32 rows of X by 256 outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
  *   -- and, if splits is not NULL, its number of K splits (1: none).
  * q4_matvec_route: the kernel variant q4_matvec (argmax == 0) or
  *   q4_lmhead_argmax (argmax != 0) runs for an N x K matrix -- "pairs_lds_g4"

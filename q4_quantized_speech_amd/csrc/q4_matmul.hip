@@ -369,8 +369,8 @@ void matmul_tile_kernel(const uint8_t* __restrict__ W, const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Wave-specialised kernel: BM x 256 tiles (BM = 128, 64 or 32; the shorter
-// tiles fill the GPU where M gives few tiles), 512 threads, K % 64 == 0.
+// Wave-specialised kernel: BM x 256 tiles (BM = 128, 96, 64 or 32; the
+// shorter tiles fill the GPU where M gives few tiles), 512 threads, K % 64 == 0.
 // Waves 0-3 multiply, each a BM x 64 slice (BM/16 x 4 MFMA tiles).  Waves 4-7 load a stage D stages ahead (each thread one weight
 // row's 36-byte block pair and 16-byte chunks of X), convert X to binary16
 // and decode the row's first block into binary16 (q - 8) d in operand order;
@@ -393,6 +393,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
                        int tiles_n, int ntiles, int split_stages) {
   constexpr int MI = BM / 16;                 // 16-row tiles of X
   constexpr int XU = BM * 16 / WS_PT;         // 16-byte X chunks per producer thread
+  static_assert(BM % 32 == 0 && BM >= 32 && BM <= 128, "X is loaded in rounds of 32 rows");
   __shared__ f16x8 As[2][2][MI][64];          // [buf][block][16-row tile][element]
   __shared__ f16x8 Bs[2][WS_BN / 16][64];     // [buf][16-row fragment][lane]: block 0, binary16
   __shared__ __attribute__((aligned(16))) uint32_t Wc[2][WS_BN * 4];  // block 1 raw codes, 4 dwords per row
@@ -929,7 +930,7 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 }  // namespace
 
 // Kernel and K-split plan for a shape.
-enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_WIDE64, MM_WIDE32, MM_TILE, MM_SIMPLE };
+enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_WIDE96, MM_WIDE64, MM_WIDE32, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
@@ -996,7 +997,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     // Estimated time (us) of (M tile, S splits): the stages of the busiest
     // workgroup slot, plus (S > 1) the partial slices and a fixed cost per
     // split call.  Fitted to encoder-shape timings: 0.92 us per 128 x 256 x 64
-    // stage, 0.7 us per 64 x 256 x 64 stage, 0.55 us per 32 x 256 x 64 stage,
+    // stage, 0.85 us per 96-row, 0.7 us per 64-row, 0.55 us per 32-row stage,
     // 0.33 us per MB of partial slices (written, then read back by the fold)
     // and 4 us for the fold's launch and the shorter pipelines.  The shorter
     // tiles win where the taller ones leave CUs idle (the 1280-wide
@@ -1005,9 +1006,9 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     double best = -1.0;
     const int64_t smax = std::min<int64_t>(MAX_SPLITS, nstg);
     const int64_t tn = (N + WS_BN - 1) / WS_BN;
-    const struct { MatmulKind k; int64_t u; double ts; } opt[3] = {
-        {MM_WIDE, ((M + 127) / 128) * tn, 0.92}, {MM_WIDE64, ((M + 63) / 64) * tn, 0.7},
-        {MM_WIDE32, ((M + 31) / 32) * tn, 0.55}};
+    const struct { MatmulKind k; int64_t u; double ts; } opt[4] = {
+        {MM_WIDE, ((M + 127) / 128) * tn, 0.92}, {MM_WIDE96, ((M + 95) / 96) * tn, 0.85},
+        {MM_WIDE64, ((M + 63) / 64) * tn, 0.7}, {MM_WIDE32, ((M + 31) / 32) * tn, 0.55}};
     for (const auto& o : opt) {
       for (int64_t sp = 1; sp <= smax; ++sp) {
         if (sp > 1 && static_cast<uint64_t>(sp * slice) > ws_bytes) break;
@@ -1042,6 +1043,7 @@ const char* matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int c
     case MM_SMALL: return "small";
     case MM_SKINNY: return "skinny";
     case MM_WIDE: return "wide128";
+    case MM_WIDE96: return "wide96";
     case MM_WIDE64: return "wide64";
     case MM_WIDE32: return "wide32";
     case MM_TILE: return "tile";
@@ -1096,13 +1098,18 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
       }
       break;
     case MM_WIDE:
+    case MM_WIDE96:
     case MM_WIDE64:
     case MM_WIDE32: {
-      const int bm = p.kind == MM_WIDE ? 128 : (p.kind == MM_WIDE64 ? 64 : 32);
+      const int bm = p.kind == MM_WIDE ? 128 : p.kind == MM_WIDE96 ? 96 : p.kind == MM_WIDE64 ? 64 : 32;
       const int tiles_n = static_cast<int>((N + WS_BN - 1) / WS_BN);
       const int ntiles = tiles_n * static_cast<int>((M + bm - 1) / bm);
       if (p.kind == MM_WIDE)
         hipLaunchKernelGGL(matmul_ws_kernel<128>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
+                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
+                           static_cast<int>(K), tiles_n, ntiles, p.stages);
+      else if (p.kind == MM_WIDE96)
+        hipLaunchKernelGGL(matmul_ws_kernel<96>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
                            w, x, y, P, static_cast<int>(M), static_cast<int>(N),
                            static_cast<int>(K), tiles_n, ntiles, p.stages);
       else if (p.kind == MM_WIDE64)

@@ -149,17 +149,20 @@ ROUTES = [
     ((76, 3072, 9216), ("skinny", None)),
     ((200, 300, 1056), ("simple", 1)),      # K % 64 == 32, binary16 path
     ((300, 256, 1024), ("tile", None)),     # narrow outputs
-    ((1500, 3840, 1280), ("wide128", 1)),   # encoder at M = 1500
+    ((1500, 3840, 1280), ("wide96", 1)),    # encoder at M = 1500
     ((1500, 1280, 1280), ("wide32", 1)),
     ((1500, 5120, 1280), ("wide128", 1)),
     ((1500, 1280, 5120), ("wide128", 4)),
-    ((375, 3072, 5120), ("wide128", 7)),    # adapter at M = 1500 / 4
+    ((375, 3072, 5120), ("wide96", 5)),     # adapter at M = 1500 / 4
     ((375, 3840, 1280), ("wide32", 1)),     # encoder at M = 375
     ((375, 5120, 1280), ("wide32", 1)),
     ((375, 1280, 1280), ("wide32", 4)),
     ((375, 1280, 5120), ("wide64", 8)),
     ((3000, 1280, 1280), ("wide64", 1)),    # encoder at M = 3000
+    ((3000, 3840, 1280), ("wide96", 1)),
+    ((3000, 5120, 1280), ("wide128", 1)),
     ((3000, 1280, 5120), ("wide128", 2)),
+    ((750, 3072, 5120), ("wide128", 3)),
 ]
 
 

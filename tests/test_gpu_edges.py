@@ -111,7 +111,9 @@ MM_CASES = [
     (4, 64, 12352, True),       # small (weights read once), K split
     (4, 64, 12352, False),      # small, no split
     (40, 300, 2048, True),      # skinny
-    (1500, 3840, 1280, True),   # wide128
+    (1500, 5120, 1280, True),   # wide128
+    (1500, 3840, 1280, True),   # wide96
+    (375, 3072, 5120, True),    # wide96 with a K split
     (1500, 1280, 1280, True),   # wide32
     (1500, 1280, 5120, True),   # wide128 with a K split
     (375, 1280, 1280, True),    # wide32 with a K split
@@ -130,8 +132,9 @@ def test_matmul_kernels_are_all_covered():
         routes.add(r)
         if sp > 1:
             routes.add(r + "+split")
-    assert routes >= {"matvec", "small", "small+split", "skinny", "wide128", "wide64", "wide32",
-                      "wide128+split", "wide64+split", "wide32+split", "tile", "simple"}, routes
+    assert routes >= {"matvec", "small", "small+split", "skinny", "wide128", "wide96", "wide64",
+                      "wide32", "wide128+split", "wide96+split", "wide64+split", "wide32+split",
+                      "tile", "simple"}, routes
 
 
 def _one_hot_rows(m, k):

@@ -251,16 +251,16 @@ __device__ __forceinline__ void am_publish(float bv, int bi, int m, void* worksp
 // SIMD) instead of living in 64 registers per lane (4 waves per SIMD).
 // G row groups of KS waves share the workgroup's x (each group stages a
 // quarter of it when G = 4) and cover 4 R G consecutive rows per pass.
-// MX rows of x per workgroup (1, or 2 for plain products): the weights are
-// read and decoded once for both rows; each row keeps its own chains in the
-// one-row order, so its results have the bits it would have alone.  A
-// missing second row (odd M) repeats the first and is never stored.
+// MX rows of x per workgroup (1 or 2): the weights are read and decoded once
+// for both rows; each row keeps its own chains in the one-row order, so its
+// results have the bits it would have alone.  A missing second row (odd M)
+// repeats the first and is never stored (nor published by the argmax).
 template <int KS, bool ARGMAX, int R, bool XL, int G, int MX>
 __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, void* workspace, int64_t N,
     int K, int M) {
-  static_assert(MX == 1 || (MX == 2 && !ARGMAX), "two rows of x only for plain products");
+  static_assert(MX == 1 || MX == 2, "one or two rows of x per workgroup");
   constexpr int ROWS = 4 * R * G;  // rows per pass
   __shared__ float red[2][KS][MX * ROWS];
   const int m = blockIdx.y * MX;  // first row of x
@@ -399,8 +399,10 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     }
   };
 
-  float bv = 0.f;
-  int bi = -1;
+  float bv[MX];
+  int bi[MX];
+#pragma unroll
+  for (int i = 0; i < MX; ++i) { bv[i] = 0.f; bi[i] = -1; }
   // Reduce the pass at r0 without branches: every lane of a DPP row holds the
   // row's sum (same bits) and writes it (same value, same address), every
   // wave adds the KS partial sums (LDS buffer q), then wave 0 consumes them:
@@ -430,11 +432,14 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     }
     if constexpr (ARGMAX) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = static_cast<int>(r0) + grp * R + r;
-        const bool take = ks == 0 && row < N && am_better(acc[0][r], row, bv, bi);
-        bv = take ? acc[0][r] : bv;
-        bi = take ? row : bi;
+      for (int i = 0; i < MX; ++i) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = static_cast<int>(r0) + grp * R + r;
+          const bool take = ks == 0 && row < N && am_better(acc[i][r], row, bv[i], bi[i]);
+          bv[i] = take ? acc[i][r] : bv[i];
+          bi[i] = take ? row : bi[i];
+        }
       }
     } else {
       const int64_t left = N - r0;  // >= 1
@@ -473,8 +478,17 @@ __global__ __launch_bounds__(64 * KS * G) void matvec_pairs_kernel(
     load(row0 + stride, wb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (ARGMAX)
-    am_publish(bv, bi, m, workspace, static_cast<int>(gridDim.x), out_idx, out_val, W, Y, N, K);
+  if constexpr (ARGMAX) {
+#pragma unroll
+    for (int i = 0; i < MX; ++i) {
+      if (i > 0) {
+        if (m + i >= M) break;  // the missing second row (uniform)
+        __syncthreads();        // the previous row's publish is done with its LDS
+      }
+      am_publish(bv[i], bi[i], m + i, workspace, static_cast<int>(gridDim.x), out_idx, out_val, W,
+                 Y, N, K);
+    }
+  }
 }
 
 // Generic kernel: any K % 32 == 0 (odd block counts, very long rows).  16
@@ -572,14 +586,15 @@ PairVariant pair_variant(int64_t N) {
   return one ? PV_REG_R1 : PV_REG_R2;
 }
 
-// Plain products with two or more rows of x take two rows per workgroup
-// (the weights are read and decoded once per pair of rows) and, with x in
-// registers, one weight row per lane (two rows of x at R = 2 would spill);
-// the argmax takes one row of x per workgroup.
+// Two or more rows of x are taken two per workgroup (the weights are read
+// and decoded once per pair of rows), with x in registers at one weight row
+// per lane (two rows of x at R = 2 would spill).  The argmax pairs rows only
+// with x in LDS (the tall tables): with x in registers its second row's
+// bookkeeping halves the occupancy.
 template <int KS, bool ARGMAX, int R, bool XL, int G>
 void launch_variant(const uint8_t* w, const float* x, float* y, int32_t* idx, float* val, void* ws,
                     int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if constexpr (!ARGMAX) {
+  if constexpr (!ARGMAX || XL) {
     if (M >= 2) {
       constexpr int R2 = XL ? R : 1;
       const PairGrid g = pair_grid<KS, ARGMAX, R2, XL, G, 2>(N);

@@ -617,3 +617,38 @@ def test_matvec_rows_as_alone(m, n, k):
     for i in range(m):
         yi = host(q4.matvec(wq, xd[i:i + 1]))[0]
         assert np.array_equal(y[i].view(np.uint32), yi.view(np.uint32)), (m, i)
+
+
+@pytest.mark.parametrize("n,k", [(65600, 1024), (65549, 3072)])
+@pytest.mark.parametrize("m", [2, 3, 5])
+def test_lmhead_rows_as_alone(m, n, k):
+    """Tall tables take the rows of x in pairs (the table is read once per
+    pair): every row gets the index and the bit-identical value of a call
+    with that row alone, the odd last row included; each index is accepted
+    by the oracle.  At M = 2 row 0 has a planted winner and row 1 a tie
+    between two identical rows (lowest index); at M > 2 every weight is
+    made non-negative and row 2 of x negative, so all of row 2's logits are
+    negative."""
+    w = _rand_w(n, k, 61 + m)
+    x = _rand_x(m, k, 62 + m)
+    if m == 2:
+        w[n - 7] = np.float32(0.02) * np.sign(x[0])
+        w[123] = w[60000] = np.float32(0.03) * np.sign(x[1])
+    else:
+        w = np.abs(w)
+        x[2] = -np.abs(x[2]) - np.float32(0.5)
+    qb = O.quantize_q4_0(w)
+    wq, xd = dev(qb), dev(x)
+    announce(f"argmax rows as alone {q4.matvec_route(n, k, argmax=True)} M={m} {n}x{k}")
+    idx, val = q4.lmhead_argmax(wq, xd)
+    idx, val = host(idx), host(val)
+    if m == 2:
+        assert int(idx[0]) == n - 7 and int(idx[1]) == 123, idx
+    for i in range(m):
+        ii, vi = q4.lmhead_argmax(wq, xd[i:i + 1])
+        assert int(host(ii)[0]) == int(idx[i]), (m, i)
+        assert host(vi)[0].view(np.uint32) == val[i].view(np.uint32), (m, i)
+        y, b = O.lmhead_logits(qb, x[i], n, k)
+        assert O.argmax_accepts(y, b, int(idx[i])), (m, i, int(idx[i]), O.argmax_lowest(y))
+        if m > 2 and i == 2:
+            assert float(val[i]) < 0.0

@@ -286,6 +286,16 @@ def main():
     lm_gbs = weight_bytes(V, D) / (us * 1e-6) / 1e9
     rows["lmhead_argmax_131072x3072"] = {"us": round(us, 3), "gbs": round(lm_gbs, 1),
                                          "frac_hbm": round(lm_gbs / HBM_PEAK_GBS, 4)}
+    # two decode streams at once: one call with two rows of x (the table is
+    # read once for both)
+    xl2 = torch.from_numpy(synth.activations(2, D, synth.seed_for(2, 3))).cuda()
+    ws2 = q4.lmhead_workspace(2, "cuda")
+    oi2 = torch.empty(2, dtype=torch.int32, device="cuda")
+    ov2 = torch.empty(2, dtype=torch.float32, device="cuda")
+    us = timed(lambda i: q4.lmhead_argmax(tables[i % rt], xl2, workspace=ws2, out_idx=oi2,
+                                          out_val=ov2, stream=stream), rt)
+    rows["lmhead_argmax_M2_131072x3072"] = {
+        "us": round(us, 3), "table_gbs": round(weight_bytes(V, D) / (us * 1e-6) / 1e9, 1)}
     ids = torch.from_numpy(synth.token_ids(synth.PREFIX_TOKENS, synth.seed_for(2, 2))).cuda()
     emb = torch.empty((synth.PREFIX_TOKENS, D), device="cuda")
     us = timed(lambda i: q4.embed_rows(tables[i % rt], ids, out=emb, stream=stream), rt)

@@ -165,7 +165,9 @@ q4_status q4_embed_rows(const void* table_q4, const int32_t* ids, float* out,
  * One launch: each workgroup folds its best (value, lowest index) into a
  * per-row key with a device-scope atomic max (order-independent, hence
  * deterministic); the last workgroup to finish writes the outputs and clears
- * the workspace.
+ * the workspace.  On tables of 65536 rows or more with K <= 4096 the rows of
+ * x are taken in pairs (the table is read once per pair); a row's index and
+ * value are those of a call with that row alone.
  *   1 <= M <= 64, 1 <= N < 2^31, K a positive multiple of 32.
  * Logits that are NaN are never selected.
  */

@@ -112,11 +112,15 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  *             planned split on the current device (0: no split planned).  A
  *             smaller workspace gives fewer splits (never an error).  Calls
  *             that share a workspace must be ordered.
- * M >= 5: weights and activations are rounded to binary16 (round to nearest
- * even) and multiplied on the matrix cores with float32 accumulation, so |x|
- * must stay below 65504, and so must every decoded weight: a block whose
+ * M >= 5: activations are rounded to binary16 (round to nearest even) and
+ * multiplied on the matrix cores with float32 accumulation, so |x| must stay
+ * below 65504.  From 5 to 16 rows with K % 64 == 0 and K <= 6144 (a short
+ * prefix, a few decode streams) the weights enter the matrix cores exactly
+ * (q - 8, the block scale applied in float32), read once by a persistent
+ * kernel with no K split.  Otherwise the decoded weights are rounded to
+ * binary16 too, so every decoded weight must stay below 65504: a block whose
  * scale exceeds 8188 in magnitude (largest |w| above 65504, which an encoder
- * only writes for weights that large) decodes to +-inf on this path.  M <= 4
+ * only writes for weights that large) decodes to +-inf there.  M <= 4
  * (several decode streams) meets the q4_matvec bound, over q4_matvec's range
  * of x: either the rows of x go through the q4_matvec
  * kernel (one or two rows, K % 64 == 32, and weights small enough that the
@@ -242,9 +246,11 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  * a shape the entry point rejects; they enqueue nothing.
  * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
  *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
- *   rows of x in pairs), "small" (M <= 4, weights read once), "skinny" (prompt
- *   prefixes), "wide128" / "wide96" / "wide64" / "wide32" (tiles of 128,
- *   96, 64 or 32 rows of X by 256 outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
+ *   rows of x in pairs), "small" (M <= 4, weights read once), "stream16"
+ *   (5 to 16 rows, K <= 6144: one MFMA tile of rows, weights read once),
+ *   "skinny" (prompt prefixes up to 80 rows), "wide128" / "wide96" /
+ *   "wide64" / "wide32" (tiles of 128, 96, 64 or 32 rows of X by 256
+ *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
  *   -- and, if splits is not NULL, its number of K splits (1: none).
  * q4_matvec_route: the kernel variant q4_matvec (argmax == 0) or
  *   q4_lmhead_argmax (argmax != 0) runs for an N x K matrix -- "pairs_lds_g4"

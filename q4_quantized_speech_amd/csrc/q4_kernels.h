@@ -41,6 +41,12 @@ int matmul_small_per_cu();
 void launch_matmul_small(const uint8_t* w, const float* x, float* y, float* P, int64_t M,
                          int64_t N, int64_t K, int splits, int pps, hipStream_t s);
 
+// 5 <= M <= 16: chunks of 256 K values per wave of the stream16 kernel
+// (0 when it does not serve the shape), and its launch (no workspace).
+int matmul_stream16_chunks(int64_t M, int64_t K);
+hipError_t launch_matmul_stream16(const uint8_t* w, const float* x, float* y, int64_t M,
+                                  int64_t N, int64_t K, int cus, hipStream_t s);
+
 hipError_t launch_embed(const uint8_t* table, const int32_t* ids, float* out, int64_t M,
                         int64_t N, int64_t K, hipStream_t s);
 

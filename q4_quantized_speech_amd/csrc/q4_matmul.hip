@@ -930,7 +930,7 @@ __global__ __launch_bounds__(S_THREADS) void matmul_simple_kernel(
 }  // namespace
 
 // Kernel and K-split plan for a shape.
-enum MatmulKind { MM_STREAM, MM_SMALL, MM_SKINNY, MM_WIDE, MM_WIDE96, MM_WIDE64, MM_WIDE32, MM_TILE, MM_SIMPLE };
+enum MatmulKind { MM_STREAM, MM_SMALL, MM_STREAM16, MM_SKINNY, MM_WIDE, MM_WIDE96, MM_WIDE64, MM_WIDE32, MM_TILE, MM_SIMPLE };
 struct MatmulPlan {
   MatmulKind kind;
   int splits;  // >= 1
@@ -942,7 +942,12 @@ struct MatmulPlan {
 // weight read once per pair) serves one or two rows, any K % 64 == 32 and
 // the shapes whose repeated weight reads stay in the caches ((M - 1) *
 // weight bytes up to STREAM_REREAD: measured faster there, it has no split
-// and no fold launch); the small-M MFMA kernel, weights read once, the rest.  Skinny for prompt-prefix row counts (bound by streaming W);
+// and no fold launch); the small-M MFMA kernel, weights read once, the rest.
+// 5 to 16 rows (one MFMA tile of rows, K <= 6144): the stream16 kernel,
+// weights read once by persistent workgroups that split K over their waves
+// (measured 12-17 % faster per decoder layer than the skinny kernel, which
+// pays per-stage costs, partial sums and a fold).  Skinny for the other
+// prompt-prefix row counts (bound by streaming W);
 // 128 x 256 wave-specialised tiles for wide outputs (half the X traffic per
 // flop of 128 x 128); 128 x 128 tiles otherwise.  K is split when the units
 // alone cannot fill every workgroup slot: at least `min_st` stages per split,
@@ -956,6 +961,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
       return MatmulPlan{MM_STREAM, 1, 0};
   }
   if (K % 64 != 0) return MatmulPlan{MM_SIMPLE, 1, 0};
+  if (matmul_stream16_chunks(M, K) > 0) return MatmulPlan{MM_STREAM16, 1, 0};
   const int nbp = static_cast<int>(K / 64);
   MatmulKind kind;
   int64_t units, slots, min_st, cap = MAX_SPLITS;
@@ -1041,6 +1047,7 @@ const char* matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int c
   switch (p.kind) {
     case MM_STREAM: return "matvec";
     case MM_SMALL: return "small";
+    case MM_STREAM16: return "stream16";
     case MM_SKINNY: return "skinny";
     case MM_WIDE: return "wide128";
     case MM_WIDE96: return "wide96";
@@ -1088,6 +1095,8 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
     case MM_SMALL:
       launch_matmul_small(w, x, y, P, M, N, K, p.splits, p.stages, s);
       break;
+    case MM_STREAM16:
+      return launch_matmul_stream16(w, x, y, M, N, K, cus, s);
     case MM_SKINNY:
       switch ((M + 15) / 16) {
         case 1: launch_skinny<1>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;

@@ -361,6 +361,224 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Five to sixteen rows of x (a short prompt prefix, a few decode streams at
+// once): the product is still an HBM stream, and one 16 x 16 x 32 MFMA per
+// weight block carries every row, so the work per weight is that of a single
+// row.  The kernel has the matvec's shape: a persistent workgroup of KS waves
+// splits K (wave w owns C consecutive 256-value chunks), holds its x in
+// registers for the whole kernel and streams 16 weight rows per pass:
+//  * x is converted once per workgroup to binary16 (round to nearest even)
+//    in the MFMA operand order (lane (m, g): row m, code group g);
+//  * lane (n, g) loads the contiguous 36-byte pair g of weight row n of each
+//    chunk (two passes in flight, double-buffered registers); the 4 x 4 lane
+//    transpose of the small-M kernel gives it code dword g of every block;
+//  * codes enter the matrix cores exactly (q - 8), one MFMA per block, and
+//    the block scale d multiplies the MFMA result in float32;
+//  * the KS waves' partial 16 x 16 tiles are added in LDS in wave order
+//    (deterministic), one barrier per pass, and written to Y.
+// No K split across workgroups, so no partial sums and no second launch.
+constexpr int MS_MAX_M = 16;
+constexpr int MS_MAX_WAVES = 16;
+
+template <int C>
+__global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
+    const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y, int M,
+    int N, int K) {
+  // x staging (one 8 KB tile per wave, in operand order), then, after a
+  // barrier, the same memory holds the passes' partial tiles
+  __shared__ f16x8 xst[MS_MAX_WAVES][512];
+  f32x4m (*red)[MS_MAX_WAVES][64] = reinterpret_cast<f32x4m (*)[MS_MAX_WAVES][64]>(&xst[0][0]);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = static_cast<int>(blockDim.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nbp = K >> 6;
+  const int rb = nbp * PAIR_BYTES;  // K <= 6144: at most 3456
+  const int units = (N + 15) >> 4;
+  // a contiguous, balanced range of 16-row units per workgroup
+  const int nwg = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  const int q = units / nwg, rem = units % nwg;
+  const int u_begin = b * q + min(b, rem);
+  const int npass = q + (b < rem ? 1 : 0);
+
+  // x operands of this wave's chunks, filled below once the first weights
+  // are requested (rows past M and values past K: zero)
+  f16x8 xa[C][8];
+  // Pair g of chunk j of weight row n of pass `pass`; rows past N, pairs past
+  // K and passes past this workgroup's range read as zeros, with no traffic.
+  auto load = [&](int pass, int j, uint32_t (&D)[9]) {
+    const int64_t row_base = static_cast<int64_t>(u_begin + pass) * 16;
+    const int rows_valid =
+        pass < npass ? static_cast<int>(min<int64_t>(16, static_cast<int64_t>(N) - row_base)) : 0;
+    const int records = rows_valid * rb;
+    const __amdgpu_buffer_rsrc_t rs = sm_rsrc(W + (pass < npass ? row_base : 0) * rb, records);
+    const int pc = 4 * (wave * C + j) + g;
+    const int vo = (n < rows_valid && pc < nbp) ? n * rb + pc * PAIR_BYTES : records;
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+    const u32x4 c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 16, 0));
+    D[0] = a.x; D[1] = a.y; D[2] = a.z; D[3] = a.w;
+    D[4] = c.x; D[5] = c.y; D[6] = c.z; D[7] = c.w;
+    D[8] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 32, 0);
+  };
+
+  // Chunk j of a pass into this wave's partial tile (rows m = 4 g + v of x,
+  // weight row n).
+  auto compute = [&](int j, const uint32_t (&D)[9], f32x4m& acc) {
+    uint32_t E[4], O[4], S[4];
+    E[0] = shift16(D[1], D[0]);
+    E[1] = shift16(D[2], D[1]);
+    E[2] = shift16(D[3], D[2]);
+    E[3] = shift16(D[4], D[3]);
+    O[0] = D[5]; O[1] = D[6]; O[2] = D[7]; O[3] = D[8];
+    const uint32_t dd = (D[0] & 0xFFFFu) | (D[4] & 0xFFFF0000u);
+    S[0] = dd; S[1] = dd; S[2] = dd; S[3] = dd;
+    transpose4(E);
+    transpose4(O);
+    transpose4(S);  // S[p] = scales of pair p of this row
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f16x8 bw = decode8_q(h ? O[p] : E[p]);
+        const f32x4m c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            xa[j][2 * p + h], bw, f32x4m{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float d = half_bits_to_float(h ? (S[p] >> 16) : (S[p] & 0xFFFFu));
+        acc.x = __builtin_fmaf(d, c.x, acc.x);
+        acc.y = __builtin_fmaf(d, c.y, acc.y);
+        acc.z = __builtin_fmaf(d, c.z, acc.z);
+        acc.w = __builtin_fmaf(d, c.w, acc.w);
+      }
+    }
+  };
+
+  // The waves' partial tiles of a pass, added in wave order, to Y's 16
+  // columns of the pass.
+  auto finish = [&](int pass, const f32x4m& acc) {
+    const int par = pass & 1;
+    red[par][wave][lane] = acc;
+    __syncthreads();
+    // output (m, nn): row m of x, weight row nn of the pass; its partials
+    // sit in lane nn + 16 (m / 4), component m % 4, of every wave (a
+    // workgroup of fewer than four waves takes the 256 outputs in turns)
+    for (int o = tid; o < 256; o += 64 * ks) {
+      const int m = o >> 4, nn = o & 15;
+      const float* src = reinterpret_cast<const float*>(&red[par][0][nn + 16 * (m >> 2)]) + (m & 3);
+      float sum = 0.f;
+      for (int w = 0; w < ks; ++w) sum += src[w * 64 * 4];
+      const int64_t col = static_cast<int64_t>(u_begin + pass) * 16 + nn;
+      if (m < M && col < N) Y[static_cast<int64_t>(m) * N + col] = sum;
+    }
+  };
+
+  // x of a chunk, eight rows at a time: each row read contiguously (lane l:
+  // values 4 l .. 4 l + 3; rows past M and values past K read as zeros,
+  // with no traffic)
+  const int xrec = M * K * 4;  // M <= 16, K <= 6144
+  const __amdgpu_buffer_rsrc_t xrs = sm_rsrc(X, xrec);
+  auto x_load = [&](int j, int m0, f32x4m (&v)[8]) {
+    const int kc = ((wave * C + j) << 8) + 4 * lane;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int m = m0 + r;
+      const int vo = (m < M && kc < K) ? 4 * (m * K + kc) : xrec;
+      v[r] = __builtin_bit_cast(f32x4m, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo, 0, 0));
+    }
+  };
+  // ... converted to binary16 and written to the wave's tile in operand
+  // order: entry (block b, row m, group g) = values 32 b + 4 g .. + 3 (bytes
+  // 0-7) and 32 b + 16 + 4 g .. + 3 (bytes 8-15), rows XOR-swizzled by b % 4
+  // so a row's 8-byte writes spread over the banks ...
+  auto x_write = [&](int m0, const f32x4m (&v)[8]) {
+    f16x8* tile = xst[wave];
+    const int wb = lane >> 3, wg = lane & 3, wh = (lane >> 2) & 1;  // this lane's block, group, half
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int m = m0 + r;
+      const f16x2 h01 = {static_cast<_Float16>(v[r].x), static_cast<_Float16>(v[r].y)};
+      const f16x2 h23 = {static_cast<_Float16>(v[r].z), static_cast<_Float16>(v[r].w)};
+      uint32_t* e = reinterpret_cast<uint32_t*>(&tile[(wb * 16 + (m ^ (wb & 3))) * 4 + wg]) + 2 * wh;
+      e[0] = __builtin_bit_cast(uint32_t, h01);
+      e[1] = __builtin_bit_cast(uint32_t, h23);
+    }
+  };
+  // ... and lane (m, g) reads its operand of each block.  The tile is the
+  // wave's own (LDS operations of a wave complete in order): no barrier.
+  auto x_read = [&](int j) {
+    const f16x8* tile = xst[wave];
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) xa[j][blk] = tile[(blk * 16 + (n ^ (blk & 3))) * 4 + g];
+  };
+
+  if constexpr (C == 1) {
+    // two passes in flight, in two register sets
+    // x first and the first two passes' weights right after: the memory
+    // counter is in order, so waiting for x never waits for the weights
+    uint32_t D0[9], D1[9];
+    {
+      f32x4m v0[8], v1[8];
+      x_load(0, 0, v0);
+      x_load(0, 8, v1);
+      load(0, 0, D0);
+      load(1, 0, D1);
+      x_write(0, v0);
+      x_write(8, v1);
+      x_read(0);
+    }
+    __syncthreads();  // every wave's operands are in registers: the tiles become partial sums
+    int i = 0;
+    for (; i + 2 <= npass; i += 2) {
+      f32x4m a0 = {0.f, 0.f, 0.f, 0.f};
+      compute(0, D0, a0);
+      load(i + 2, 0, D0);
+      finish(i, a0);
+      f32x4m a1 = {0.f, 0.f, 0.f, 0.f};
+      compute(0, D1, a1);
+      load(i + 3, 0, D1);
+      finish(i + 1, a1);
+    }
+    if (i < npass) {
+      f32x4m a0 = {0.f, 0.f, 0.f, 0.f};
+      compute(0, D0, a0);
+      finish(i, a0);
+    }
+  } else {
+    // one register set per chunk: a chunk's next-pass load is issued as soon
+    // as the chunk is computed, so C chunks are in flight during a pass
+    uint32_t D[C][9];
+    {
+      f32x4m v0[8], v1[8];
+      x_load(0, 0, v0);
+      x_load(0, 8, v1);
+#pragma unroll
+      for (int j = 0; j < C; ++j) load(0, j, D[j]);
+      x_write(0, v0);
+      x_write(8, v1);
+      x_read(0);
+      // the later chunks eight rows at a time (registers: the earlier
+      // chunks' operands and the weights are live)
+#pragma unroll
+      for (int j = 1; j < C; ++j) {
+        x_load(j, 0, v0);
+        x_write(0, v0);
+        x_load(j, 8, v0);
+        x_write(8, v0);
+        x_read(j);
+      }
+    }
+    __syncthreads();  // every wave's operands are in registers: the tiles become partial sums
+    for (int i = 0; i < npass; ++i) {
+      f32x4m a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        compute(j, D[j], a);
+        load(i + 1, j, D[j]);
+      }
+      finish(i, a);
+    }
+  }
+}
+
 }  // namespace
 
 // Workgroups of the small-M kernel resident on one CU.
@@ -376,6 +594,58 @@ int matmul_small_per_cu() {
     cache.store(per_cu, std::memory_order_relaxed);
   }
   return per_cu;
+}
+
+// The stream16 kernel's chunks per wave for K (0: not served).  Up to 16
+// chunks one wave each; up to 24 (K = 6144) in 12 waves of up to 2.  Longer
+// rows stay with the skinny kernel: three chunks per wave fit in registers,
+// but every workgroup then reads more x (M x K floats) than the weights of
+// its passes; measured slower than the skinny kernel on the 3072 x 9216
+// down projection at 5 to 16 rows (13-14 against 11-12 us).
+int matmul_stream16_chunks(int64_t M, int64_t K) {
+  if (M < 5 || M > MS_MAX_M || K % 64 != 0 || K <= 0) return 0;
+  const int64_t nchunk = (K + 255) / 256;
+  if (nchunk <= MS_MAX_WAVES) return 1;
+  return nchunk <= 24 ? 2 : 0;
+}
+
+template <int C>
+static int stream16_per_cu(int threads) {
+  // per process and block size (resource use is fixed); racing first calls
+  // store the same value
+  static std::atomic<int> cache[MS_MAX_WAVES + 1];
+  const int w = threads / 64;
+  int per_cu = cache[w].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    int nb = 0;
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matmul_stream16_kernel<C>, threads, 0);
+    per_cu = (e == hipSuccess && nb > 0) ? nb : 1;
+    cache[w].store(per_cu, std::memory_order_relaxed);
+  }
+  return per_cu;
+}
+
+hipError_t launch_matmul_stream16(const uint8_t* w, const float* x, float* y, int64_t M,
+                                  int64_t N, int64_t K, int cus, hipStream_t s) {
+  const int C = matmul_stream16_chunks(M, K);
+  if (C == 0) return hipErrorInvalidValue;
+  const int64_t nchunk = (K + 255) / 256;
+  const int ks = static_cast<int>((nchunk + C - 1) / C);
+  const int threads = 64 * ks;
+  const int64_t units = (N + 15) / 16;
+  const int per_cu = C == 1 ? stream16_per_cu<1>(threads) : stream16_per_cu<2>(threads);
+  const int64_t slots = static_cast<int64_t>(per_cu) * cus;
+  // the fewest passes per workgroup that fit, spread evenly
+  const int64_t passes = (units + slots - 1) / slots;
+  const unsigned grid = static_cast<unsigned>((units + passes - 1) / passes);
+  if (C == 1)
+    hipLaunchKernelGGL(matmul_stream16_kernel<1>, dim3(grid), dim3(threads), 0, s, w, x, y,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  else
+    hipLaunchKernelGGL(matmul_stream16_kernel<2>, dim3(grid), dim3(threads), 0, s, w, x, y,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  return hipGetLastError();
 }
 
 void launch_matmul_small(const uint8_t* w, const float* x, float* y, float* P, int64_t M,

@@ -145,7 +145,11 @@ ROUTES = [
     ((4, 18432, 3072), ("small", None)),    # four streams, large W: weights read once
     ((2, 64, 12352), ("small", None)),      # K > 12288: beyond the pair kernel
     ((3, 300, 1056), ("matvec", 1)),        # K % 64 == 32 keeps the float32 path
-    ((16, 18432, 3072), ("skinny", None)),  # prompt prefix
+    ((16, 18432, 3072), ("stream16", 1)),   # prompt prefix up to 16 rows: one MFMA tile
+    ((5, 3072, 4096), ("stream16", 1)),
+    ((8, 3072, 6144), ("stream16", 1)),     # two 256-value chunks per wave
+    ((16, 3072, 9216), ("skinny", None)),   # K past 6144: x would outweigh the weights
+    ((17, 18432, 3072), ("skinny", None)),  # past one MFMA tile of rows
     ((76, 3072, 9216), ("skinny", None)),
     ((200, 300, 1056), ("simple", 1)),      # K % 64 == 32, binary16 path
     ((300, 256, 1024), ("tile", None)),     # narrow outputs

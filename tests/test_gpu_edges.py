@@ -110,6 +110,7 @@ MM_CASES = [
     (2, 64, 3072, False),       # matvec kernel (rows in pairs)
     (4, 64, 12352, True),       # small (weights read once), K split
     (4, 64, 12352, False),      # small, no split
+    (8, 300, 2048, True),       # stream16 (5 to 16 rows, no split)
     (40, 300, 2048, True),      # skinny
     (1500, 5120, 1280, True),   # wide128
     (1500, 3840, 1280, True),   # wide96
@@ -132,7 +133,7 @@ def test_matmul_kernels_are_all_covered():
         routes.add(r)
         if sp > 1:
             routes.add(r + "+split")
-    assert routes >= {"matvec", "small", "small+split", "skinny", "wide128", "wide96", "wide64",
+    assert routes >= {"matvec", "small", "small+split", "stream16", "skinny", "wide128", "wide96", "wide64",
                       "wide32", "wide128+split", "wide96+split", "wide64+split", "wide32+split",
                       "tile", "simple"}, routes
 
@@ -148,16 +149,18 @@ def _one_hot_rows(m, k):
 
 @pytest.mark.parametrize("m,n,k,ws", MM_CASES)
 def test_subnormal_scales_matmul_one_hot(m, n, k, ws):
-    """Y[i, :] = column cols[i] of the decoded weights: exactly on the float32
-    routes (M <= 4), its binary16 rounding on the matrix-core routes."""
+    """Y[i, :] = column cols[i] of the decoded weights: exactly on the routes
+    whose weights enter unrounded (M <= 4, and the stream16 kernel's q - 8
+    with the scale applied in float32), its binary16 rounding on the other
+    matrix-core routes."""
     qb = subnormal_table(n, k, 5 * m + n + k)
     wd = O.dequantize_q4_0(qb, n, k)
     x, cols = _one_hot_rows(m, k)
     want = wd[:, cols].T + 0.0                      # -0 -> +0
-    exact = m <= 4
+    route = q4.matmul_route(m, n, k, int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) if ws else 0)
+    exact = m <= 4 or route[0] == "stream16"
     if not exact:
         want = O.round_f16(want) + 0.0
-    route = q4.matmul_route(m, n, k, int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) if ws else 0)
     announce(f"subnormal one-hot matmul {route} {m}x{n}x{k}")
     y = host(q4.matmul(dev(qb), dev(x), workspace=True if ws else None)) + 0.0
     bad = y.view(np.uint32) != want.view(np.uint32)

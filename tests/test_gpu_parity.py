@@ -255,7 +255,7 @@ def test_matmul_parity_small(m, n, k):
     assert_within(y, ref, b, *MF, f"matmul {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(100, 200, 4096), (16, 3072, 9216), (129, 130, 1024),
+@pytest.mark.parametrize("m,n,k", [(100, 200, 4096), (17, 3072, 9216), (129, 130, 1024),
                                    (1, 64, 640)])
 def test_matmul_split_k(m, n, k):
     """K split over several workgroups per tile: with the planned workspace, a

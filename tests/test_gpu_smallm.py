@@ -4,7 +4,8 @@ x in pairs; one or two rows, K % 64 == 32, weights whose repeated reads stay
 in the caches) and the small-M kernel (weights read once and multiplied on the matrix
 cores with exact q - 8 operands, the block scales applied in float32 and x
 carried as two binary16 parts; K > 12288 always takes it).  Row counts just
-past it (5 to 16) take the binary16 kernels and are held to the binary16
+past it (5 to 16) take binary16 x (the stream16 kernel: weights exact, read
+once, one MFMA per block for all the rows) and are held to the binary16
 bound.
 Shapes follow the decoder of the model the pages run (section "Architecture" of
 "Implémentation en Rust du modèle Voxtral Mini 4B Realtime de Mistral pour
@@ -130,6 +131,33 @@ def test_small_m_deterministic_and_in_bounds():
     assert np.all(host(out)[m * n:] == sentinel)
     q4.matmul(qb, x, out=out[: m * n].view(m, n), workspace=ws[: need // 4].view(torch.uint8))
     assert np.array_equal(host(out)[: m * n].view(np.uint32), first.view(np.uint32))
+
+
+@pytest.mark.parametrize("m", [5, 9, 16])
+@pytest.mark.parametrize("n,k", [(1, 64), (17, 256), (33, 4352), (300, 4096), (31, 6080),
+                                 (40, 6144)])
+def test_stream16_edges(m, n, k):
+    """5 to 16 rows of x on the stream16 kernel, at its edges: a workgroup of
+    one wave (K = 64: the 256 outputs of a pass taken in turns), one full
+    chunk, 17 chunks (two per wave, the last wave's second chunk empty), 16
+    waves of one chunk, a last chunk cut short, 24 chunks in 12 waves; N not
+    a multiple of the 16 weight rows of a pass.  No workspace is planned, the
+    same bits come back on a repeat, and nothing past Y is written."""
+    assert q4.matmul_route(m, n, k, 1 << 30) == ("stream16", 1)
+    assert int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) == 0
+    qb = _w(n, k, 31 * m + n + k)
+    x = synth.activations(m, k, 19 + m + k)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    sentinel = -12345.0
+    out = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
+    announce(f"stream16 edge {m}x{n}x{k}")
+    q4.matmul(wq, xd, out=out[: m * n].view(m, n))
+    first = host(out)
+    assert np.all(first[m * n:] == sentinel)
+    assert_within(first[: m * n].reshape(m, n), ref, b, *MF, f"stream16 {m}x{n}x{k}")
+    q4.matmul(wq, xd, out=out[: m * n].view(m, n))
+    assert np.array_equal(host(out).view(np.uint32), first.view(np.uint32))
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 3072, 4096),

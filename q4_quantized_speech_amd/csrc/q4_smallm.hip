@@ -503,11 +503,16 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
     }
   };
   // ... and lane (m, g) reads its operand of each block.  The tile is the
-  // wave's own (LDS operations of a wave complete in order): no barrier.
+  // wave's own and LDS operations of a wave complete in order, so no barrier
+  // is needed; the empty asm statements with a memory clobber keep the
+  // compiler from moving these reads across the tile's writes (which go
+  // through another type) on either side.
   auto x_read = [&](int j) {
     const f16x8* tile = xst[wave];
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) xa[j][blk] = tile[(blk * 16 + (n ^ (blk & 3))) * 4 + g];
+    __asm__ volatile("" ::: "memory");
   };
 
   if constexpr (C == 1) {

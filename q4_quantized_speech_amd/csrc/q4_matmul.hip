@@ -106,6 +106,15 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 constexpr int T_BM = 128;
 constexpr int MAX_SPLITS = 16;
 
+// Cache policy of the GEMMs' output stores (Y, or the K split's partial
+// slices): sc0 sc1, written through to memory as they are produced rather
+// than left dirty in the L2 for the end of the kernel.  Measured on the
+// wide kernel (same box, alternating builds): encoder layer + adapter at
+// M = 1500 125.8-129.3 -> 121.9 us, at M = 375 78.7 -> 76.2, at M = 3000
+// 226.7 -> 221.7; on Y alone it gained little (125.0 at M = 1500), so most
+// of it is the partial slices that the fold kernel reads next.
+constexpr int WRITE_THROUGH = 17;  // the sc0 and sc1 bits of the buffer instruction
+
 // Raw buffer resource over [base, base + bytes): 32-bit data, range checked,
 // so loads past the end return zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -474,7 +483,8 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float val = acc[i][j][v];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0,
+                                                  WRITE_THROUGH);
           }
         }
       }

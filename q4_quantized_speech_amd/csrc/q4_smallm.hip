@@ -362,33 +362,37 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Five to sixteen rows of x (a short prompt prefix, a few decode streams at
-// once): the product is still an HBM stream, and one 16 x 16 x 32 MFMA per
-// weight block carries every row, so the work per weight is that of a single
-// row.  The kernel has the matvec's shape: a persistent workgroup of KS waves
-// splits K (wave w owns C consecutive 256-value chunks), holds its x in
-// registers for the whole kernel and streams 16 weight rows per pass:
+// Five to 48 rows of x (a short prompt prefix, a few decode streams at once):
+// the product is still an HBM stream, and one 16 x 16 x 32 MFMA per weight
+// block and 16 rows of x carries them, so the work per weight is nearly that
+// of a single row.  The kernel has the matvec's shape: a persistent
+// workgroup of KS waves splits K (wave w owns C consecutive 256-value
+// chunks), holds its x in registers for the whole kernel and streams 16
+// weight rows per pass:
 //  * x is converted once per workgroup to binary16 (round to nearest even)
-//    in the MFMA operand order (lane (m, g): row m, code group g);
+//    in the MFMA operand order (lane (m, g): row m of a 16-row tile of x,
+//    code group g), MT tiles of 16 rows;
 //  * lane (n, g) loads the contiguous 36-byte pair g of weight row n of each
 //    chunk (two passes in flight, double-buffered registers); the 4 x 4 lane
 //    transpose of the small-M kernel gives it code dword g of every block;
-//  * codes enter the matrix cores exactly (q - 8), one MFMA per block, and
-//    the block scale d multiplies the MFMA result in float32;
+//  * codes enter the matrix cores exactly (q - 8), one MFMA per block and
+//    tile of x, and the block scale d multiplies the MFMA result in float32;
 //  * the KS waves' partial 16 x 16 tiles are added in LDS in wave order
 //    (deterministic), one barrier per pass, and written to Y.
 // No K split across workgroups, so no partial sums and no second launch.
-constexpr int MS_MAX_M = 16;
+constexpr int MS_MAX_MT = 3;   // tiles of 16 rows of x
 constexpr int MS_MAX_WAVES = 16;
 
-template <int C>
-__global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
+template <int C, int MT>
+__global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream16_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y, int M,
     int N, int K) {
+  static_assert(MT >= 1 && MT <= MS_MAX_MT && (C == 1 || MT == 1), "registers: see the host side");
   // x staging (one 8 KB tile per wave, in operand order), then, after a
   // barrier, the same memory holds the passes' partial tiles
   __shared__ f16x8 xst[MS_MAX_WAVES][512];
-  f32x4m (*red)[MS_MAX_WAVES][64] = reinterpret_cast<f32x4m (*)[MS_MAX_WAVES][64]>(&xst[0][0]);
+  f32x4m (*red)[MT][MS_MAX_WAVES][64] =
+      reinterpret_cast<f32x4m (*)[MT][MS_MAX_WAVES][64]>(&xst[0][0]);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = static_cast<int>(blockDim.x >> 6);
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
 
   // x operands of this wave's chunks, filled below once the first weights
   // are requested (rows past M and values past K: zero)
-  f16x8 xa[C][8];
+  f16x8 xa[C][MT][8];
   // Pair g of chunk j of weight row n of pass `pass`; rows past N, pairs past
   // K and passes past this workgroup's range read as zeros, with no traffic.
   auto load = [&](int pass, int j, uint32_t (&D)[9]) {
@@ -422,9 +426,9 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
     D[8] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 32, 0);
   };
 
-  // Chunk j of a pass into this wave's partial tile (rows m = 4 g + v of x,
-  // weight row n).
-  auto compute = [&](int j, const uint32_t (&D)[9], f32x4m& acc) {
+  // Chunk j of a pass into this wave's partial tiles (tile t: rows
+  // m = 16 t + 4 g + v of x, weight row n).
+  auto compute = [&](int j, const uint32_t (&D)[9], f32x4m (&acc)[MT]) {
     uint32_t E[4], O[4], S[4];
     E[0] = shift16(D[1], D[0]);
     E[1] = shift16(D[2], D[1]);
@@ -440,32 +444,48 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
     for (int p = 0; p < 4; ++p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const f16x8 bw = decode8_q(h ? O[p] : E[p]);
-        const f32x4m c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            xa[j][2 * p + h], bw, f32x4m{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float d = half_bits_to_float(h ? (S[p] >> 16) : (S[p] & 0xFFFFu));
-        acc.x = __builtin_fmaf(d, c.x, acc.x);
-        acc.y = __builtin_fmaf(d, c.y, acc.y);
-        acc.z = __builtin_fmaf(d, c.z, acc.z);
-        acc.w = __builtin_fmaf(d, c.w, acc.w);
+        const uint32_t dbits = h ? (S[p] >> 16) : (S[p] & 0xFFFFu);
+        if constexpr (MT == 1) {
+          // exact weights: q - 8 into the MFMA, d applied to its result
+          const f16x8 bw = decode8_q(h ? O[p] : E[p]);
+          const float d = half_bits_to_float(dbits);
+          const f32x4m c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              xa[j][0][2 * p + h], bw, f32x4m{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc[0].x = __builtin_fmaf(d, c.x, acc[0].x);
+          acc[0].y = __builtin_fmaf(d, c.y, acc[0].y);
+          acc[0].z = __builtin_fmaf(d, c.z, acc[0].z);
+          acc[0].w = __builtin_fmaf(d, c.w, acc[0].w);
+        } else {
+          // two or three tiles of x: (q - 8) d rounded once to binary16 (as
+          // on the skinny and wide routes) and accumulated in the MFMA; the
+          // exact form's float32 products would not fit in the registers
+          const _Float16 dh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(dbits));
+          const f16x8 bw = decode8_q(h ? O[p] : E[p]) * dh;
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[j][t][2 * p + h], bw, acc[t], 0, 0, 0);
+        }
       }
     }
   };
 
   // The waves' partial tiles of a pass, added in wave order, to Y's 16
   // columns of the pass.
-  auto finish = [&](int pass, const f32x4m& acc) {
+  auto finish = [&](int pass, const f32x4m (&acc)[MT]) {
     const int par = pass & 1;
-    red[par][wave][lane] = acc;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[par][t][wave][lane] = acc[t];
     __syncthreads();
-    // output (m, nn): row m of x, weight row nn of the pass; its partials
-    // sit in lane nn + 16 (m / 4), component m % 4, of every wave (a
-    // workgroup of fewer than four waves takes the 256 outputs in turns)
-    for (int o = tid; o < 256; o += 64 * ks) {
-      const int m = o >> 4, nn = o & 15;
-      const float* src = reinterpret_cast<const float*>(&red[par][0][nn + 16 * (m >> 2)]) + (m & 3);
+    // output (m, nn): row m = 16 t + mm of x, weight row nn of the pass; its
+    // partials sit in tile t, lane nn + 16 (mm / 4), component mm % 4, of
+    // every wave (workgroups of fewer threads than outputs take them in turns)
+    for (int o = tid; o < 256 * MT; o += 64 * ks) {
+      const int t = o >> 8, mm = (o >> 4) & 15, nn = o & 15;
+      const float* src =
+          reinterpret_cast<const float*>(&red[par][t][0][nn + 16 * (mm >> 2)]) + (mm & 3);
       float sum = 0.f;
       for (int w = 0; w < ks; ++w) sum += src[w * 64 * 4];
+      const int m = 16 * t + mm;
       const int64_t col = static_cast<int64_t>(u_begin + pass) * 16 + nn;
       if (m < M && col < N) Y[static_cast<int64_t>(m) * N + col] = sum;
     }
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
   // x of a chunk, eight rows at a time: each row read contiguously (lane l:
   // values 4 l .. 4 l + 3; rows past M and values past K read as zeros,
   // with no traffic)
-  const int xrec = M * K * 4;  // M <= 16, K <= 6144
+  const int xrec = M * K * 4;  // M <= 48, K <= 6144
   const __amdgpu_buffer_rsrc_t xrs = sm_rsrc(X, xrec);
   auto x_load = [&](int j, int m0, f32x4m (&v)[8]) {
     const int kc = ((wave * C + j) << 8) + 4 * lane;
@@ -486,15 +506,16 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
     }
   };
   // ... converted to binary16 and written to the wave's tile in operand
-  // order: entry (block b, row m, group g) = values 32 b + 4 g .. + 3 (bytes
-  // 0-7) and 32 b + 16 + 4 g .. + 3 (bytes 8-15), rows XOR-swizzled by b % 4
-  // so a row's 8-byte writes spread over the banks ...
-  auto x_write = [&](int m0, const f32x4m (&v)[8]) {
+  // order: entry (block b, row m of the 16-row tile, group g) = values
+  // 32 b + 4 g .. + 3 (bytes 0-7) and 32 b + 16 + 4 g .. + 3 (bytes 8-15),
+  // rows XOR-swizzled by b % 4 so a row's 8-byte writes spread over the
+  // banks (lr0: the first of the eight rows within the tile) ...
+  auto x_write = [&](int lr0, const f32x4m (&v)[8]) {
     f16x8* tile = xst[wave];
     const int wb = lane >> 3, wg = lane & 3, wh = (lane >> 2) & 1;  // this lane's block, group, half
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int m = m0 + r;
+      const int m = lr0 + r;
       const f16x2 h01 = {static_cast<_Float16>(v[r].x), static_cast<_Float16>(v[r].y)};
       const f16x2 h23 = {static_cast<_Float16>(v[r].z), static_cast<_Float16>(v[r].w)};
       uint32_t* e = reinterpret_cast<uint32_t*>(&tile[(wb * 16 + (m ^ (wb & 3))) * 4 + wg]) + 2 * wh;
@@ -507,18 +528,19 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
   // is needed; the empty asm statements with a memory clobber keep the
   // compiler from moving these reads across the tile's writes (which go
   // through another type) on either side.
-  auto x_read = [&](int j) {
+  auto x_read = [&](int j, int t) {
     const f16x8* tile = xst[wave];
     __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) xa[j][blk] = tile[(blk * 16 + (n ^ (blk & 3))) * 4 + g];
+    for (int blk = 0; blk < 8; ++blk) xa[j][t][blk] = tile[(blk * 16 + (n ^ (blk & 3))) * 4 + g];
     __asm__ volatile("" ::: "memory");
   };
 
   if constexpr (C == 1) {
-    // two passes in flight, in two register sets
-    // x first and the first two passes' weights right after: the memory
-    // counter is in order, so waiting for x never waits for the weights
+    // two passes in flight, in two register sets; x first and the first two
+    // passes' weights right after (the memory counter is in order, so
+    // waiting for x never waits for the weights), the later tiles of x
+    // eight rows at a time
     uint32_t D0[9], D1[9];
     {
       f32x4m v0[8], v1[8];
@@ -528,22 +550,36 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
       load(1, 0, D1);
       x_write(0, v0);
       x_write(8, v1);
-      x_read(0);
+      x_read(0, 0);
+#pragma unroll
+      for (int t = 1; t < MT; ++t) {
+        x_load(0, 16 * t, v0);
+        x_write(0, v0);
+        x_load(0, 16 * t + 8, v0);
+        x_write(8, v0);
+        x_read(0, t);
+      }
     }
     __syncthreads();  // every wave's operands are in registers: the tiles become partial sums
     int i = 0;
     for (; i + 2 <= npass; i += 2) {
-      f32x4m a0 = {0.f, 0.f, 0.f, 0.f};
+      f32x4m a0[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) a0[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
       compute(0, D0, a0);
       load(i + 2, 0, D0);
       finish(i, a0);
-      f32x4m a1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4m a1[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) a1[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
       compute(0, D1, a1);
       load(i + 3, 0, D1);
       finish(i + 1, a1);
     }
     if (i < npass) {
-      f32x4m a0 = {0.f, 0.f, 0.f, 0.f};
+      f32x4m a0[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) a0[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
       compute(0, D0, a0);
       finish(i, a0);
     }
@@ -559,7 +595,7 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
       for (int j = 0; j < C; ++j) load(0, j, D[j]);
       x_write(0, v0);
       x_write(8, v1);
-      x_read(0);
+      x_read(0, 0);
       // the later chunks eight rows at a time (registers: the earlier
       // chunks' operands and the weights are live)
 #pragma unroll
@@ -568,12 +604,14 @@ __global__ __launch_bounds__(C == 1 ? 1024 : 768) void matmul_stream16_kernel(
         x_write(0, v0);
         x_load(j, 8, v0);
         x_write(8, v0);
-        x_read(j);
+        x_read(j, 0);
       }
     }
     __syncthreads();  // every wave's operands are in registers: the tiles become partial sums
     for (int i = 0; i < npass; ++i) {
-      f32x4m a = {0.f, 0.f, 0.f, 0.f};
+      f32x4m a[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) a[t] = f32x4m{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         compute(j, D[j], a);
@@ -601,20 +639,24 @@ int matmul_small_per_cu() {
   return per_cu;
 }
 
-// The stream16 kernel's chunks per wave for K (0: not served).  Up to 16
-// chunks one wave each; up to 24 (K = 6144) in 12 waves of up to 2.  Longer
-// rows stay with the skinny kernel: three chunks per wave fit in registers,
-// but every workgroup then reads more x (M x K floats) than the weights of
-// its passes; measured slower than the skinny kernel on the 3072 x 9216
-// down projection at 5 to 16 rows (13-14 against 11-12 us).
+// The stream16 kernel's shape for (M, K): chunks of 256 K values per wave
+// and tiles of 16 rows of x (0: not served).  One tile (M <= 16): up to 16
+// chunks one wave each, or up to 24 (K = 6144) in 12 waves of two.  Two or
+// three tiles (M <= 48): up to 12 chunks (K = 3072), one per wave (the x
+// operands of 48 rows fill 96 registers).  Longer rows stay with the skinny
+// kernel: three chunks per wave fit in registers at one tile, but every
+// workgroup then reads more x (M x K floats) than the weights of its
+// passes; measured slower than the skinny kernel on the 3072 x 9216 down
+// projection at 5 to 16 rows (13-14 against 11-12 us).
 int matmul_stream16_chunks(int64_t M, int64_t K) {
-  if (M < 5 || M > MS_MAX_M || K % 64 != 0 || K <= 0) return 0;
+  if (M < 5 || M > 16 * MS_MAX_MT || K % 64 != 0 || K <= 0) return 0;
   const int64_t nchunk = (K + 255) / 256;
+  if (M > 16) return nchunk <= 12 ? 1 : 0;
   if (nchunk <= MS_MAX_WAVES) return 1;
   return nchunk <= 24 ? 2 : 0;
 }
 
-template <int C>
+template <int C, int MT>
 static int stream16_per_cu(int threads) {
   // per process and block size (resource use is fixed); racing first calls
   // store the same value
@@ -623,33 +665,41 @@ static int stream16_per_cu(int threads) {
   int per_cu = cache[w].load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
-    const hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, matmul_stream16_kernel<C>, threads, 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, matmul_stream16_kernel<C, MT>, threads, 0);
     per_cu = (e == hipSuccess && nb > 0) ? nb : 1;
     cache[w].store(per_cu, std::memory_order_relaxed);
   }
   return per_cu;
 }
 
+template <int C, int MT>
+static void launch_stream16(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
+                            int64_t K, int ks, int cus, hipStream_t s) {
+  const int threads = 64 * ks;
+  const int64_t units = (N + 15) / 16;
+  const int64_t slots = static_cast<int64_t>(stream16_per_cu<C, MT>(threads)) * cus;
+  // the fewest passes per workgroup that fit, spread evenly
+  const int64_t passes = (units + slots - 1) / slots;
+  const unsigned grid = static_cast<unsigned>((units + passes - 1) / passes);
+  hipLaunchKernelGGL((matmul_stream16_kernel<C, MT>), dim3(grid), dim3(threads), 0, s, w, x, y,
+                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+}
+
 hipError_t launch_matmul_stream16(const uint8_t* w, const float* x, float* y, int64_t M,
                                   int64_t N, int64_t K, int cus, hipStream_t s) {
   const int C = matmul_stream16_chunks(M, K);
   if (C == 0) return hipErrorInvalidValue;
-  const int64_t nchunk = (K + 255) / 256;
-  const int ks = static_cast<int>((nchunk + C - 1) / C);
-  const int threads = 64 * ks;
-  const int64_t units = (N + 15) / 16;
-  const int per_cu = C == 1 ? stream16_per_cu<1>(threads) : stream16_per_cu<2>(threads);
-  const int64_t slots = static_cast<int64_t>(per_cu) * cus;
-  // the fewest passes per workgroup that fit, spread evenly
-  const int64_t passes = (units + slots - 1) / slots;
-  const unsigned grid = static_cast<unsigned>((units + passes - 1) / passes);
-  if (C == 1)
-    hipLaunchKernelGGL(matmul_stream16_kernel<1>, dim3(grid), dim3(threads), 0, s, w, x, y,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  const int ks = static_cast<int>(((K + 255) / 256 + C - 1) / C);
+  const int64_t mt = (M + 15) / 16;
+  if (C == 2)
+    launch_stream16<2, 1>(w, x, y, M, N, K, ks, cus, s);
+  else if (mt == 1)
+    launch_stream16<1, 1>(w, x, y, M, N, K, ks, cus, s);
+  else if (mt == 2)
+    launch_stream16<1, 2>(w, x, y, M, N, K, ks, cus, s);
   else
-    hipLaunchKernelGGL(matmul_stream16_kernel<2>, dim3(grid), dim3(threads), 0, s, w, x, y,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+    launch_stream16<1, 3>(w, x, y, M, N, K, ks, cus, s);
   return hipGetLastError();
 }
 

@@ -149,7 +149,10 @@ ROUTES = [
     ((5, 3072, 4096), ("stream16", 1)),
     ((8, 3072, 6144), ("stream16", 1)),     # two 256-value chunks per wave
     ((16, 3072, 9216), ("skinny", None)),   # K past 6144: x would outweigh the weights
-    ((17, 18432, 3072), ("skinny", None)),  # past one MFMA tile of rows
+    ((17, 18432, 3072), ("stream16", 1)),   # two tiles of 16 rows of x, K <= 3072
+    ((38, 6144, 3072), ("stream16", 1)),    # the 38-token prefix: three tiles
+    ((38, 3072, 4096), ("skinny", None)),   # more than one tile and K past 3072
+    ((49, 18432, 3072), ("skinny", None)),  # past three tiles
     ((76, 3072, 9216), ("skinny", None)),
     ((200, 300, 1056), ("simple", 1)),      # K % 64 == 32, binary16 path
     ((300, 256, 1024), ("tile", None)),     # narrow outputs

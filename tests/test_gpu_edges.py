@@ -110,8 +110,9 @@ MM_CASES = [
     (2, 64, 3072, False),       # matvec kernel (rows in pairs)
     (4, 64, 12352, True),       # small (weights read once), K split
     (4, 64, 12352, False),      # small, no split
-    (8, 300, 2048, True),       # stream16 (5 to 16 rows, no split)
-    (40, 300, 2048, True),      # skinny
+    (8, 300, 2048, True),       # stream16 (5 to 16 rows, no split; exact weights)
+    (20, 300, 2048, True),      # stream16 with two tiles of x (binary16 weights)
+    (40, 300, 4096, True),      # skinny (more than one tile of x and K past 3072)
     (1500, 5120, 1280, True),   # wide128
     (1500, 3840, 1280, True),   # wide96
     (375, 3072, 5120, True),    # wide96 with a K split
@@ -151,14 +152,14 @@ def _one_hot_rows(m, k):
 def test_subnormal_scales_matmul_one_hot(m, n, k, ws):
     """Y[i, :] = column cols[i] of the decoded weights: exactly on the routes
     whose weights enter unrounded (M <= 4, and the stream16 kernel's q - 8
-    with the scale applied in float32), its binary16 rounding on the other
-    matrix-core routes."""
+    with the scale applied in float32 up to 16 rows), its binary16 rounding
+    on the other matrix-core routes."""
     qb = subnormal_table(n, k, 5 * m + n + k)
     wd = O.dequantize_q4_0(qb, n, k)
     x, cols = _one_hot_rows(m, k)
     want = wd[:, cols].T + 0.0                      # -0 -> +0
     route = q4.matmul_route(m, n, k, int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) if ws else 0)
-    exact = m <= 4 or route[0] == "stream16"
+    exact = m <= 4 or (route[0] == "stream16" and m <= 16)
     if not exact:
         want = O.round_f16(want) + 0.0
     announce(f"subnormal one-hot matmul {route} {m}x{n}x{k}")

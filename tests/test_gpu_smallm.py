@@ -160,6 +160,29 @@ def test_stream16_edges(m, n, k):
     assert np.array_equal(host(out).view(np.uint32), first.view(np.uint32))
 
 
+@pytest.mark.parametrize("m", [17, 32, 33, 38, 48])
+@pytest.mark.parametrize("n,k", [(1, 64), (17, 256), (300, 3072), (31, 2880), (70, 1216)])
+def test_stream16_tiles_edges(m, n, k):
+    """17 to 48 rows of x on the stream16 kernel: two or three tiles of 16
+    rows (the last one partly past M), one wave per 256-value chunk up to
+    K = 3072, a last chunk cut short, N not a multiple of 16; the binary16
+    bound, the same bits on a repeat, nothing written past Y."""
+    assert q4.matmul_route(m, n, k, 1 << 30) == ("stream16", 1)
+    qb = _w(n, k, 37 * m + n + k)
+    x = synth.activations(m, k, 23 + m + k)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    sentinel = -12345.0
+    out = torch.full((m * n + 64,), sentinel, dtype=torch.float32, device="cuda")
+    announce(f"stream16 tiles {m}x{n}x{k}")
+    q4.matmul(wq, xd, out=out[: m * n].view(m, n))
+    first = host(out)
+    assert np.all(first[m * n:] == sentinel)
+    assert_within(first[: m * n].reshape(m, n), ref, b, *MF, f"stream16 tiles {m}x{n}x{k}")
+    q4.matmul(wq, xd, out=out[: m * n].view(m, n))
+    assert np.array_equal(host(out).view(np.uint32), first.view(np.uint32))
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 3072, 4096),
                                    (3, 65, 1056), (2, 18432, 3072), (2, 65536, 3072),
                                    (2, 3072, 9216)])

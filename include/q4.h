@@ -117,8 +117,10 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  * below 65504.  From 5 to 16 rows with K % 64 == 0 and K <= 6144 (a short
  * prefix, a few decode streams) the weights enter the matrix cores exactly
  * (q - 8, the block scale applied in float32), read once by a persistent
- * kernel with no K split.  Otherwise the decoded weights are rounded to
- * binary16 too, so every decoded weight must stay below 65504: a block whose
+ * kernel with no K split; from 17 to 48 rows with K <= 3072 the same kernel
+ * takes the decoded weights rounded to binary16.  Everywhere but on the
+ * exact route the decoded weights are rounded to binary16, so every decoded
+ * weight must stay below 65504: a block whose
  * scale exceeds 8188 in magnitude (largest |w| above 65504, which an encoder
  * only writes for weights that large) decodes to +-inf there.  M <= 4
  * (several decode streams) meets the q4_matvec bound, over q4_matvec's range
@@ -247,8 +249,9 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
  *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
  *   rows of x in pairs), "small" (M <= 4, weights read once), "stream16"
- *   (5 to 16 rows, K <= 6144: one MFMA tile of rows, weights read once),
- *   "skinny" (prompt prefixes up to 80 rows), "wide128" / "wide96" /
+ *   (5 to 16 rows with K <= 6144, or up to 48 rows with K <= 3072: tiles of
+ *   16 rows of x, weights read once), "skinny" (prompt prefixes up to 80
+ *   rows), "wide128" / "wide96" /
  *   "wide64" / "wide32" (tiles of 128, 96, 64 or 32 rows of X by 256
  *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
  *   -- and, if splits is not NULL, its number of K splits (1: none).

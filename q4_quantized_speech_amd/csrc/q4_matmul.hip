@@ -953,11 +953,11 @@ struct MatmulPlan {
 // the shapes whose repeated weight reads stay in the caches ((M - 1) *
 // weight bytes up to STREAM_REREAD: measured faster there, it has no split
 // and no fold launch); the small-M MFMA kernel, weights read once, the rest.
-// 5 to 16 rows (one MFMA tile of rows, K <= 6144): the stream16 kernel,
-// weights read once by persistent workgroups that split K over their waves
-// (measured 12-17 % faster per decoder layer than the skinny kernel, which
-// pays per-stage costs, partial sums and a fold).  Skinny for the other
-// prompt-prefix row counts (bound by streaming W);
+// 5 to 16 rows with K <= 6144, or up to 48 rows with K <= 3072: the
+// stream16 kernel, weights read once by persistent workgroups that split K
+// over their waves (measured 7-17 % faster per decoder layer than the
+// skinny kernel, which pays per-stage costs, partial sums and a fold).
+// Skinny for the other prompt-prefix shapes (bound by streaming W);
 // 128 x 256 wave-specialised tiles for wide outputs (half the X traffic per
 // flop of 128 x 128); 128 x 128 tiles otherwise.  K is split when the units
 // alone cannot fill every workgroup slot: at least `min_st` stages per split,

@@ -966,6 +966,9 @@ struct MatmulPlan {
 constexpr int64_t STREAM_REREAD = int64_t{40} << 20;
 static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   if (M <= 4) {
+    // three or four rows, K <= 6144: the stream16 kernel with x in two
+    // binary16 parts (the q4_matvec bound), weights read once
+    if (M >= 3 && matmul_stream16_chunks(M, K) > 0) return MatmulPlan{MM_STREAM16, 1, 0};
     const int64_t wbytes = N * (K / 32) * 18;
     if (M == 1 || K % 64 != 0 || (K <= 12288 && (M == 2 || (M - 1) * wbytes <= STREAM_REREAD)))
       return MatmulPlan{MM_STREAM, 1, 0};

@@ -383,11 +383,21 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 constexpr int MS_MAX_MT = 3;   // tiles of 16 rows of x
 constexpr int MS_MAX_WAVES = 16;
 
-template <int C, int MT>
+// HL (three or four rows of x, the q4_matvec bound): x is carried as two
+// binary16 parts, hi = RN(x s) and lo = RN(x s - hi), with s the power of two
+// that puts the largest magnitude of the row's 256-value chunk in
+// [2^14, 2^15) (undone in float32 after the chunk): hi in rows 0-3 of the
+// tile, lo in rows 4-7, so one MFMA per block carries both; a chunk whose
+// nonzero magnitudes span more than 2^20 (or whose largest reaches 2^124, or
+// is not finite) is "wide": its operands are zero and its products are added
+// with float32 FMAs of the centred codes against x read again from memory,
+// the rule and the arithmetic of the small-M kernel.
+template <int C, int MT, bool HL>
 __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream16_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y, int M,
     int N, int K) {
   static_assert(MT >= 1 && MT <= MS_MAX_MT && (C == 1 || MT == 1), "registers: see the host side");
+  static_assert(!HL || MT == 1, "two-part x: one tile");
   // x staging (one 8 KB tile per wave, in operand order), then, after a
   // barrier, the same memory holds the passes' partial tiles
   __shared__ f16x8 xst[MS_MAX_WAVES][512];
@@ -409,6 +419,12 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
   // x operands of this wave's chunks, filled below once the first weights
   // are requested (rows past M and values past K: zero)
   f16x8 xa[C][MT][8];
+  // HL: per chunk, 2^-s of each row of x and the mask of its wide rows
+  // (the same in every lane of the wave)
+  float xu[C][4];
+  uint32_t xwide[C];
+  const int xrec = M * K * 4;  // M <= 48, K <= 6144
+  const __amdgpu_buffer_rsrc_t xrs = sm_rsrc(X, xrec);
   // Pair g of chunk j of weight row n of pass `pass`; rows past N, pairs past
   // K and passes past this workgroup's range read as zeros, with no traffic.
   auto load = [&](int pass, int j, uint32_t (&D)[9]) {
@@ -440,6 +456,7 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
     transpose4(E);
     transpose4(O);
     transpose4(S);  // S[p] = scales of pair p of this row
+    f32x4m cacc = {0.f, 0.f, 0.f, 0.f};  // one tile, exact weights: this chunk's sum
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
 #pragma unroll
@@ -451,10 +468,10 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
           const float d = half_bits_to_float(dbits);
           const f32x4m c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               xa[j][0][2 * p + h], bw, f32x4m{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          acc[0].x = __builtin_fmaf(d, c.x, acc[0].x);
-          acc[0].y = __builtin_fmaf(d, c.y, acc[0].y);
-          acc[0].z = __builtin_fmaf(d, c.z, acc[0].z);
-          acc[0].w = __builtin_fmaf(d, c.w, acc[0].w);
+          cacc.x = __builtin_fmaf(d, c.x, cacc.x);
+          cacc.y = __builtin_fmaf(d, c.y, cacc.y);
+          cacc.z = __builtin_fmaf(d, c.z, cacc.z);
+          cacc.w = __builtin_fmaf(d, c.w, cacc.w);
         } else {
           // two or three tiles of x: (q - 8) d rounded once to binary16 (as
           // on the skinny and wide routes) and accumulated in the MFMA; the
@@ -467,6 +484,53 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
         }
       }
     }
+    if constexpr (MT == 1 && !HL) {
+      acc[0] += cacc;
+    } else if constexpr (HL) {
+      // lane groups 0 and 1 hold the hi and lo sums of row v of x: undo the
+      // chunk's scaling of that row (groups 2 and 3 hold zero rows)
+      acc[0].x = __builtin_fmaf(cacc.x, xu[j][0], acc[0].x);
+      acc[0].y = __builtin_fmaf(cacc.y, xu[j][1], acc[0].y);
+      acc[0].z = __builtin_fmaf(cacc.z, xu[j][2], acc[0].z);
+      acc[0].w = __builtin_fmaf(cacc.w, xu[j][3], acc[0].w);
+      // wide rows of this chunk (rare; the mask is the same for the whole
+      // wave): the lane's 8 codes of each block against the float32 x,
+      // centred codes, the block scale per block; the four lane groups' sums
+      // are added in a fixed order and land in lane group 0 (the hi rows)
+      if (xwide[j] != 0u) {
+        const int kb = (wave * C + j) << 8;
+        // one row at a time, not unrolled (the rare path must not raise the
+        // register count of the common one)
+#pragma unroll 1
+        for (int r = 0; r < 4; ++r) {
+          if ((xwide[j] >> r) & 1u) {
+            float part = 0.f;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int k0 = kb + 64 * p + 32 * h + 4 * g;
+                const int vo = k0 < K ? 4 * (r * K + k0) : xrec;
+                const f32x4 xl = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo, 0, 0));
+                const f32x4 xh = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo, 64, 0));
+                const float d = half_bits_to_float(h ? (S[p] >> 16) : (S[p] & 0xFFFFu));
+                part = __builtin_fmaf(d, nib_dot4_centred(h ? O[p] : E[p], xl, xh, 0.f), part);
+                // one block at a time: the rare path must not raise the
+                // register count of the common one by hoisting its loads
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const float add = g == 0 ? part : 0.f;
+            acc[0].x += r == 0 ? add : 0.f;
+            acc[0].y += r == 1 ? add : 0.f;
+            acc[0].z += r == 2 ? add : 0.f;
+            acc[0].w += r == 3 ? add : 0.f;
+          }
+        }
+      }
+    }
   };
 
   // The waves' partial tiles of a pass, added in wave order, to Y's 16
@@ -476,6 +540,23 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
 #pragma unroll
     for (int t = 0; t < MT; ++t) red[par][t][wave][lane] = acc[t];
     __syncthreads();
+    if constexpr (HL) {
+      // output (m, nn), m < 4: the hi sum (lane nn) and the lo sum (lane
+      // nn + 16), component m, each over the waves in wave order
+      for (int o = tid; o < 64; o += 64 * ks) {
+        const int m = o >> 4, nn = o & 15;
+        const float* sh = reinterpret_cast<const float*>(&red[par][0][0][nn]) + m;
+        const float* sl = reinterpret_cast<const float*>(&red[par][0][0][nn + 16]) + m;
+        float hi = 0.f, lo = 0.f;
+        for (int w = 0; w < ks; ++w) {
+          hi += sh[w * 64 * 4];
+          lo += sl[w * 64 * 4];
+        }
+        const int64_t col = static_cast<int64_t>(u_begin + pass) * 16 + nn;
+        if (m < M && col < N) Y[static_cast<int64_t>(m) * N + col] = hi + lo;
+      }
+      return;
+    }
     // output (m, nn): row m = 16 t + mm of x, weight row nn of the pass; its
     // partials sit in tile t, lane nn + 16 (mm / 4), component mm % 4, of
     // every wave (workgroups of fewer threads than outputs take them in turns)
@@ -494,8 +575,6 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
   // x of a chunk, eight rows at a time: each row read contiguously (lane l:
   // values 4 l .. 4 l + 3; rows past M and values past K read as zeros,
   // with no traffic)
-  const int xrec = M * K * 4;  // M <= 48, K <= 6144
-  const __amdgpu_buffer_rsrc_t xrs = sm_rsrc(X, xrec);
   auto x_load = [&](int j, int m0, f32x4m (&v)[8]) {
     const int kc = ((wave * C + j) << 8) + 4 * lane;
 #pragma unroll
@@ -523,6 +602,63 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
       e[1] = __builtin_bit_cast(uint32_t, h23);
     }
   };
+  // HL: rows 0-3 of x (the rest zero) as hi (tile rows 0-3) and lo (tile
+  // rows 4-7) after the chunk's power-of-two scaling of each row; a wide
+  // row's operands are zero and its bit is set in xwide[j].  The maxima and
+  // minima are wave reductions (one chunk is one wave), so every branch on
+  // them is uniform.
+  auto x_write_hl = [&](int j, const f32x4m (&v)[8]) {
+    f16x8* tile = xst[wave];
+    const int wb = lane >> 3, wg = lane & 3, wh = (lane >> 2) & 1;
+    uint32_t wm = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4m av = {fabsf(v[r].x), fabsf(v[r].y), fabsf(v[r].z), fabsf(v[r].w)};
+      const float a = fmaxf(fmaxf(av.x, av.y), fmaxf(av.z, av.w));
+      // smallest nonzero magnitude (+inf when all four are zero; NaN never
+      // counts, in neither reduction)
+      float z = __builtin_inff();
+      z = av.x > 0.f ? fminf(z, av.x) : z;
+      z = av.y > 0.f ? fminf(z, av.y) : z;
+      z = av.z > 0.f ? fminf(z, av.z) : z;
+      z = av.w > 0.f ? fminf(z, av.w) : z;
+      const float cmax = wave_max_nonneg(a);
+      const float cmin = wave_min_nonneg(z);
+      const bool wide = !(cmax < 0x1p124f) || cmin < cmax * 0x1p-20f;
+      const int se = scale_exp(__float_as_uint(cmax));
+      xu[j][r] = exp2i(-se);
+      uint32_t hw0 = 0u, hw1 = 0u, lw0 = 0u, lw1 = 0u;
+      if (wide) {
+        wm |= 1u << r;
+      } else {
+        const f32x4m xv = v[r] * exp2i(se);
+        const f16x2 h01 = {static_cast<_Float16>(xv.x), static_cast<_Float16>(xv.y)};
+        const f16x2 h23 = {static_cast<_Float16>(xv.z), static_cast<_Float16>(xv.w)};
+        const f16x2 l01 = {static_cast<_Float16>(xv.x - static_cast<float>(h01[0])),
+                           static_cast<_Float16>(xv.y - static_cast<float>(h01[1]))};
+        const f16x2 l23 = {static_cast<_Float16>(xv.z - static_cast<float>(h23[0])),
+                           static_cast<_Float16>(xv.w - static_cast<float>(h23[1]))};
+        hw0 = __builtin_bit_cast(uint32_t, h01);
+        hw1 = __builtin_bit_cast(uint32_t, h23);
+        lw0 = __builtin_bit_cast(uint32_t, l01);
+        lw1 = __builtin_bit_cast(uint32_t, l23);
+      }
+      uint32_t* eh = reinterpret_cast<uint32_t*>(&tile[(wb * 16 + (r ^ (wb & 3))) * 4 + wg]) + 2 * wh;
+      uint32_t* el =
+          reinterpret_cast<uint32_t*>(&tile[(wb * 16 + ((4 + r) ^ (wb & 3))) * 4 + wg]) + 2 * wh;
+      eh[0] = hw0;
+      eh[1] = hw1;
+      el[0] = lw0;
+      el[1] = lw1;
+    }
+#pragma unroll
+    for (int m = 8; m < 16; ++m) {
+      uint32_t* e = reinterpret_cast<uint32_t*>(&tile[(wb * 16 + (m ^ (wb & 3))) * 4 + wg]) + 2 * wh;
+      e[0] = 0u;
+      e[1] = 0u;
+    }
+    xwide[j] = wm;
+  };
   // ... and lane (m, g) reads its operand of each block.  The tile is the
   // wave's own and LDS operations of a wave complete in order, so no barrier
   // is needed; the empty asm statements with a memory clobber keep the
@@ -545,11 +681,15 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
     {
       f32x4m v0[8], v1[8];
       x_load(0, 0, v0);
-      x_load(0, 8, v1);
+      if constexpr (!HL) x_load(0, 8, v1);
       load(0, 0, D0);
       load(1, 0, D1);
-      x_write(0, v0);
-      x_write(8, v1);
+      if constexpr (HL) {
+        x_write_hl(0, v0);
+      } else {
+        x_write(0, v0);
+        x_write(8, v1);
+      }
       x_read(0, 0);
 #pragma unroll
       for (int t = 1; t < MT; ++t) {
@@ -590,20 +730,28 @@ __global__ __launch_bounds__(C == 1 && MT == 1 ? 1024 : 768) void matmul_stream1
     {
       f32x4m v0[8], v1[8];
       x_load(0, 0, v0);
-      x_load(0, 8, v1);
+      if constexpr (!HL) x_load(0, 8, v1);
 #pragma unroll
       for (int j = 0; j < C; ++j) load(0, j, D[j]);
-      x_write(0, v0);
-      x_write(8, v1);
+      if constexpr (HL) {
+        x_write_hl(0, v0);
+      } else {
+        x_write(0, v0);
+        x_write(8, v1);
+      }
       x_read(0, 0);
       // the later chunks eight rows at a time (registers: the earlier
       // chunks' operands and the weights are live)
 #pragma unroll
       for (int j = 1; j < C; ++j) {
         x_load(j, 0, v0);
-        x_write(0, v0);
-        x_load(j, 8, v0);
-        x_write(8, v0);
+        if constexpr (HL) {
+          x_write_hl(j, v0);
+        } else {
+          x_write(0, v0);
+          x_load(j, 8, v0);
+          x_write(8, v0);
+        }
         x_read(j, 0);
       }
     }
@@ -649,14 +797,14 @@ int matmul_small_per_cu() {
 // passes; measured slower than the skinny kernel on the 3072 x 9216 down
 // projection at 5 to 16 rows (13-14 against 11-12 us).
 int matmul_stream16_chunks(int64_t M, int64_t K) {
-  if (M < 5 || M > 16 * MS_MAX_MT || K % 64 != 0 || K <= 0) return 0;
+  if (M < 3 || M > 16 * MS_MAX_MT || K % 64 != 0 || K <= 0) return 0;
   const int64_t nchunk = (K + 255) / 256;
   if (M > 16) return nchunk <= 12 ? 1 : 0;
   if (nchunk <= MS_MAX_WAVES) return 1;
   return nchunk <= 24 ? 2 : 0;
 }
 
-template <int C, int MT>
+template <int C, int MT, bool HL>
 static int stream16_per_cu(int threads) {
   // per process and block size (resource use is fixed); racing first calls
   // store the same value
@@ -666,23 +814,23 @@ static int stream16_per_cu(int threads) {
   if (per_cu == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, matmul_stream16_kernel<C, MT>, threads, 0);
+        &nb, matmul_stream16_kernel<C, MT, HL>, threads, 0);
     per_cu = (e == hipSuccess && nb > 0) ? nb : 1;
     cache[w].store(per_cu, std::memory_order_relaxed);
   }
   return per_cu;
 }
 
-template <int C, int MT>
+template <int C, int MT, bool HL>
 static void launch_stream16(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
                             int64_t K, int ks, int cus, hipStream_t s) {
   const int threads = 64 * ks;
   const int64_t units = (N + 15) / 16;
-  const int64_t slots = static_cast<int64_t>(stream16_per_cu<C, MT>(threads)) * cus;
+  const int64_t slots = static_cast<int64_t>(stream16_per_cu<C, MT, HL>(threads)) * cus;
   // the fewest passes per workgroup that fit, spread evenly
   const int64_t passes = (units + slots - 1) / slots;
   const unsigned grid = static_cast<unsigned>((units + passes - 1) / passes);
-  hipLaunchKernelGGL((matmul_stream16_kernel<C, MT>), dim3(grid), dim3(threads), 0, s, w, x, y,
+  hipLaunchKernelGGL((matmul_stream16_kernel<C, MT, HL>), dim3(grid), dim3(threads), 0, s, w, x, y,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
 }
 
@@ -692,14 +840,20 @@ hipError_t launch_matmul_stream16(const uint8_t* w, const float* x, float* y, in
   if (C == 0) return hipErrorInvalidValue;
   const int ks = static_cast<int>(((K + 255) / 256 + C - 1) / C);
   const int64_t mt = (M + 15) / 16;
-  if (C == 2)
-    launch_stream16<2, 1>(w, x, y, M, N, K, ks, cus, s);
-  else if (mt == 1)
-    launch_stream16<1, 1>(w, x, y, M, N, K, ks, cus, s);
-  else if (mt == 2)
-    launch_stream16<1, 2>(w, x, y, M, N, K, ks, cus, s);
-  else
-    launch_stream16<1, 3>(w, x, y, M, N, K, ks, cus, s);
+  if (M <= 4) {
+    if (C == 2)
+      launch_stream16<2, 1, true>(w, x, y, M, N, K, ks, cus, s);
+    else
+      launch_stream16<1, 1, true>(w, x, y, M, N, K, ks, cus, s);
+  } else if (C == 2) {
+    launch_stream16<2, 1, false>(w, x, y, M, N, K, ks, cus, s);
+  } else if (mt == 1) {
+    launch_stream16<1, 1, false>(w, x, y, M, N, K, ks, cus, s);
+  } else if (mt == 2) {
+    launch_stream16<1, 2, false>(w, x, y, M, N, K, ks, cus, s);
+  } else {
+    launch_stream16<1, 3, false>(w, x, y, M, N, K, ks, cus, s);
+  }
   return hipGetLastError();
 }
 

@@ -142,7 +142,10 @@ ROUTES = [
     ((1, 18432, 3072), ("matvec", 1)),      # decode step
     ((2, 18432, 3072), ("matvec", 1)),      # two streams: a pair of rows reads W once
     ((2, 131072, 3072), ("matvec", 1)),     # at any size
-    ((4, 18432, 3072), ("small", None)),    # four streams, large W: weights read once
+    ((4, 18432, 3072), ("stream16", 1)),    # four streams: x in two binary16 parts, weights once
+    ((3, 3072, 4096), ("stream16", 1)),
+    ((4, 3072, 9216), ("small", None)),     # K past 6144, large W: the small-M kernel
+    ((4, 300, 6208), ("matvec", 1)),        # 25 chunks, small W: rows through the matvec
     ((2, 64, 12352), ("small", None)),      # K > 12288: beyond the pair kernel
     ((3, 300, 1056), ("matvec", 1)),        # K % 64 == 32 keeps the float32 path
     ((16, 18432, 3072), ("stream16", 1)),   # prompt prefix up to 16 rows: one MFMA tile

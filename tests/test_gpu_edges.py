@@ -110,6 +110,7 @@ MM_CASES = [
     (2, 64, 3072, False),       # matvec kernel (rows in pairs)
     (4, 64, 12352, True),       # small (weights read once), K split
     (4, 64, 12352, False),      # small, no split
+    (4, 300, 2048, False),      # stream16, x in two binary16 parts (the matvec bound)
     (8, 300, 2048, True),       # stream16 (5 to 16 rows, no split; exact weights)
     (20, 300, 2048, True),      # stream16 with two tiles of x (binary16 weights)
     (40, 300, 4096, True),      # skinny (more than one tile of x and K past 3072)

@@ -1,9 +1,11 @@
 """q4_matmul with 1 to 4 rows of x meets the matvec bound (1e-4 * B + 1e-6),
-not only the binary16 one, on both of its routes: the matvec kernel (rows of
-x in pairs; one or two rows, K % 64 == 32, weights whose repeated reads stay
-in the caches) and the small-M kernel (weights read once and multiplied on the matrix
-cores with exact q - 8 operands, the block scales applied in float32 and x
-carried as two binary16 parts; K > 12288 always takes it).  Row counts just
+not only the binary16 one, on each of its routes: the matvec kernel (rows of
+x in pairs; one or two rows, K % 64 == 32, and K past 6144 with weights whose
+repeated reads stay in the caches), the stream16 kernel for three or four
+rows with K <= 6144 and the small-M kernel for the rest (both read the
+weights once and multiply them on the matrix cores as exact q - 8 operands,
+the block scales applied in float32 and x carried as two binary16 parts
+after a power-of-two scaling per 256-value chunk).  Row counts just
 past it (5 to 16) take binary16 x (the stream16 kernel: weights exact, read
 once, one MFMA per block for all the rows) and are held to the binary16
 bound.
@@ -54,13 +56,14 @@ def test_small_m_matvec_bound(m, n, k):
         assert_within(y, ref, b, *_bound(m), f"small-M {m}x{n}x{k} ws={ws is not None}")
 
 
-@pytest.mark.parametrize("k", [1280, 12352])
+@pytest.mark.parametrize("k", [1280, 4352, 12352])
 @pytest.mark.parametrize("case", ["tiny", "huge", "spread", "zero_row", "mixed_rows",
                                   "outlier_1e9", "outlier_1e11", "outlier_1e30", "outlier_3e38",
                                   "huge_3e35", "tiny_among_normal"])
 def test_small_m_x_range(case, k):
-    """x far from 1 keeps the bound on both routes (K = 12352: the small-M
-    kernel's per-chunk power-of-two scaling): all tiny, all huge (past
+    """x far from 1 keeps the bound on the routes with a per-chunk
+    power-of-two scaling of x (K = 1280 and 4352: the stream16 kernel with
+    one and two chunks per wave; K = 12352: the small-M kernel): all tiny, all huge (past
     binary16's range), one large value among small ones, a row of zeros, rows
     of very different magnitudes; huge values on zero-weight columns (they
     set a chunk's scale but add nothing, so the chunk's other values must
@@ -95,7 +98,7 @@ def test_small_m_x_range(case, k):
     qb = O.quantize_q4_0(w)
     x = x.astype(np.float32)
     ref, b = O.matmul_f64(qb, x, n, k)
-    announce(f"small-M x range {case} k={k}")
+    announce(f"small-M x range {case} k={k} route={q4.matmul_route(m, n, k, 0)}")
     y = host(q4.matmul(dev(qb), dev(x)))
     assert_within(y, ref, b, *MV, f"x range {case}")
     if case == "zero_row":
@@ -183,7 +186,7 @@ def test_stream16_tiles_edges(m, n, k):
     assert np.array_equal(host(out).view(np.uint32), first.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 3072, 4096),
+@pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 300, 6208),
                                    (3, 65, 1056), (2, 18432, 3072), (2, 65536, 3072),
                                    (2, 3072, 9216)])
 def test_small_m_stream_route_is_matvec(m, n, k):

@@ -252,8 +252,8 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
  *   rows of x in pairs), "small" (M <= 4, weights read once), "stream16"
  *   (3 to 16 rows with K <= 6144, or up to 48 rows with K <= 3072: tiles of
- *   16 rows of x, weights read once), "skinny" (prompt prefixes up to 80
- *   rows), "wide128" / "wide96" /
+ *   16 rows of x, weights read once), "skinny" (the other prompt-prefix
+ *   shapes up to 48 rows), "wide128" / "wide96" /
  *   "wide64" / "wide32" (tiles of 128, 96, 64 or 32 rows of X by 256
  *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)
  *   -- and, if splits is not NULL, its number of K splits (1: none).

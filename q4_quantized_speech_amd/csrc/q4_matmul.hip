@@ -17,11 +17,13 @@
 //
 // Kernels, by shape (the planner at the end of this file picks one): the
 // wave-specialised kernel for outputs at least 512 wide (the encoder and the
-// adapter: BM x 256 tiles, loading waves decode, multiplying waves only read
-// LDS), the skinny kernel for 5 to 80 rows of X (prompt prefixes: W streams
-// through the MFMA A operand), the tile kernel below for narrower outputs,
-// the simple kernel for K % 64 == 32; up to 4 rows of X go to the matvec or
-// to the small-M kernel (q4_smallm.hip).
+// adapter, and prompt prefixes past 48 rows: BM x 256 tiles, loading waves
+// decode, multiplying waves only read LDS), the skinny kernel for the
+// prompt-prefix shapes up to 48 rows that the stream16 kernel does not take
+// (W streams through the MFMA A operand), the tile kernel below for narrower
+// outputs, the simple kernel for K % 64 == 32; up to 4 rows of X go to the
+// matvec or to the small-M kernel, 3 to 48 rows mostly to the stream16
+// kernel (q4_smallm.hip).
 //
 // Tile kernel (K % 64 == 0): a 256-thread workgroup owns a 128 x 128 tile of
 // Y; each of its four waves a 64 x 64 sub-tile (4 x 4 MFMA tiles).  K
@@ -594,7 +596,7 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel: M <= 16 MT rows of X (MT <= 5), K % 64 == 0.  The decoder's
+// Skinny kernel: M <= 16 MT rows of X (MT <= 3), K % 64 == 0.  The decoder's
 // prompt prefix (16 / 38 / 76 tokens) is far below a 128-row tile, and the
 // product is bound by streaming W; so W is the MFMA A operand (16 weight rows
 // per wave, decoded straight into operand registers) and X^T the B operand,
@@ -611,7 +613,13 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 // n = 4 (lane / 16) + v, so each lane writes 4 consecutive columns of Y.
 // ---------------------------------------------------------------------------
 constexpr int SK_ROWS = 128, SK_THREADS = 512;
-constexpr int SK_MAX_MT = 5;
+constexpr int SK_MAX_MT = 3;
+// Rows of x up to which q4_matmul routes to the skinny kernel (its three
+// tiles of 16 rows; it once served up to 80).  Past 48 rows the wide kernel's planner won on
+// the decoder shapes (same box, 76 rows: QKV 17.0 vs 18.3 us, O 14.7 vs
+// 16.0, gate+up 25.6 vs 32.0, down 20.6 vs 22.1); at 38 rows the skinny
+// kernel was ahead or within 2 %.
+constexpr int SK_ROUTE_MAX_M = 16 * SK_MAX_MT;
 // Block pairs per stage: 4 up to 32 rows of X; beyond that the binary16 X^T
 // of 4 pairs would leave one workgroup per CU (LDS), so 2.  A ring of two
 // register sets.
@@ -989,7 +997,7 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     slots = (2 * units > cus ? static_cast<int64_t>(matmul_small_per_cu()) : 1) *
             static_cast<int64_t>(cus);
     min_st = 4;
-  } else if (M <= 16 * SK_MAX_MT) {
+  } else if (M <= SK_ROUTE_MAX_M) {
     kind = MM_SKINNY;
     units = (N + SK_ROWS - 1) / SK_ROWS;
     // one workgroup per CU, two when the row groups alone fill half the CUs
@@ -1116,9 +1124,7 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
       switch ((M + 15) / 16) {
         case 1: launch_skinny<1>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
         case 2: launch_skinny<2>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
-        case 3: launch_skinny<3>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
-        case 4: launch_skinny<4>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
-        default: launch_skinny<5>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
+        default: launch_skinny<3>(w, x, y, P, M, N, K, p.splits, p.stages, s); break;
       }
       break;
     case MM_WIDE:

@@ -155,8 +155,9 @@ ROUTES = [
     ((17, 18432, 3072), ("stream16", 1)),   # two tiles of 16 rows of x, K <= 3072
     ((38, 6144, 3072), ("stream16", 1)),    # the 38-token prefix: three tiles
     ((38, 3072, 4096), ("skinny", None)),   # more than one tile and K past 3072
-    ((49, 18432, 3072), ("skinny", None)),  # past three tiles
-    ((76, 3072, 9216), ("skinny", None)),
+    ((49, 18432, 3072), ("wide64", 3)),     # past three tiles: the wide kernel
+    ((76, 3072, 9216), ("wide96", 16)),     # past 48 rows: the wide kernel's planner
+    ((48, 3072, 4096), ("skinny", None)),   # up to 48 rows with K past 3072: skinny
     ((200, 300, 1056), ("simple", 1)),      # K % 64 == 32, binary16 path
     ((300, 256, 1024), ("tile", None)),     # narrow outputs
     ((1500, 3840, 1280), ("wide96", 1)),    # encoder at M = 1500

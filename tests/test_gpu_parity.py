@@ -280,11 +280,11 @@ def test_matmul_split_k(m, n, k):
 @pytest.mark.parametrize("m", [1, 16, 17, 32, 33, 48, 80, 81])
 @pytest.mark.parametrize("n,k", [(100, 128), (257, 2048), (130, 640), (70, 192), (33, 64)])
 def test_matmul_skinny_edges(m, n, k):
-    """Row counts at the skinny kernel's tile edges (16 per MFMA tile, up to
-    80; up to 32 rows a stage is four block pairs, so K of 1, 2, 3, 10 pairs
-    ends in a partial stage) and just past it (81 goes to the 128-row tiles);
-    ragged N; with the planned workspace (K split where planned) and without
-    one."""
+    """Row counts at the 16-row MFMA tile edges of the skinny and stream16
+    kernels (up to 48 rows; up to 32 rows a skinny stage is four block pairs,
+    so K of 1, 2, 3, 10 pairs ends in a partial stage) and past them (80 and
+    81 rows go to the tile kernel at these widths); ragged N; with the
+    planned workspace (K split where planned) and without one."""
     qb = O.quantize_q4_0(_rand_w(n, k, 7 * m + n + k))
     x = _rand_x(m, k, 5 + m)
     ref, b = O.matmul_f64(qb, x, n, k)

@@ -362,21 +362,27 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Five to 48 rows of x (a short prompt prefix, a few decode streams at once):
-// the product is still an HBM stream, and one 16 x 16 x 32 MFMA per weight
-// block and 16 rows of x carries them, so the work per weight is nearly that
-// of a single row.  The kernel has the matvec's shape: a persistent
-// workgroup of KS waves splits K (wave w owns C consecutive 256-value
-// chunks), holds its x in registers for the whole kernel and streams 16
-// weight rows per pass:
+// Three to 48 rows of x (a short prompt prefix, a few decode streams at
+// once): the product is still an HBM stream, and one 16 x 16 x 32 MFMA per
+// weight block and 16 rows of x carries them, so the work per weight is
+// nearly that of a single row.  The kernel has the matvec's shape: a
+// persistent workgroup of KS waves splits K (wave w owns C consecutive
+// 256-value chunks), holds its x in registers for the whole kernel and
+// streams 16 weight rows per pass:
 //  * x is converted once per workgroup to binary16 (round to nearest even)
 //    in the MFMA operand order (lane (m, g): row m of a 16-row tile of x,
-//    code group g), MT tiles of 16 rows;
+//    code group g), MT tiles of 16 rows; for three or four rows (HL) as two
+//    binary16 parts in one tile, described below;
 //  * lane (n, g) loads the contiguous 36-byte pair g of weight row n of each
-//    chunk (two passes in flight, double-buffered registers); the 4 x 4 lane
-//    transpose of the small-M kernel gives it code dword g of every block;
-//  * codes enter the matrix cores exactly (q - 8), one MFMA per block and
-//    tile of x, and the block scale d multiplies the MFMA result in float32;
+//    chunk (at one chunk per wave two passes in flight in two register
+//    sets, at two a chunk's next load issued as soon as it is computed);
+//    the 4 x 4 lane transpose of the small-M kernel gives it code dword g
+//    of every block;
+//  * with one tile of x the codes enter the matrix cores exactly (q - 8),
+//    one MFMA per block, and the block scale d multiplies the MFMA result in
+//    float32; with two or three tiles (q - 8) d rounded once to binary16 is
+//    accumulated in the MFMA (the float32 products would not fit in the
+//    registers);
 //  * the KS waves' partial 16 x 16 tiles are added in LDS in wave order
 //    (deterministic), one barrier per pass, and written to Y.
 // No K split across workgroups, so no partial sums and no second launch.

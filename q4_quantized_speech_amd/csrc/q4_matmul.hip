@@ -1041,6 +1041,11 @@ static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t w
     for (const auto& o : opt) {
       for (int64_t sp = 1; sp <= smax; ++sp) {
         if (sp > 1 && static_cast<uint64_t>(sp * slice) > ws_bytes) break;
+        // prompt prefixes (HBM bound): no more partial bytes than weight
+        // bytes, the skinny kernel's rule (the model alone chose 96-row
+        // tiles split 8 for QKV at 76 rows, 19.2 us, where 64-row tiles
+        // split 5 measured 17.0)
+        if (sp > 1 && M <= 80 && sp * slice > N * (K / 32) * 18) break;
         const int64_t per = (nstg + sp - 1) / sp;
         const int64_t rounds = (o.u * sp + slots - 1) / slots;
         double est = o.ts * static_cast<double>(per * rounds);

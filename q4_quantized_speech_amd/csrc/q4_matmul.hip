@@ -509,6 +509,11 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
   } else {
     // ------------------------------- prepare -------------------------------
     const int tp = tid - WS_CONS;  // 0 .. 255
+    // On tiles of up to 96 rows the loading waves' stage (loads, convert,
+    // decode, LDS writes) is as long as the multiplying waves' MFMAs: issue
+    // ahead of them on the shared SIMDs (measured, same box: M = 375 encoder
+    // layer 83.5 -> 81.5 us; on 128-row tiles it cost ~1 %, so not there).
+    if constexpr (BM <= 96) __builtin_amdgcn_s_setprio(3);
     // X: one A-operand entry per round -- elements 4g..4g+3 and 16+4g..+3 of
     // block xb of row xr + 32 u (two 16-byte loads, one 16-byte LDS write;
     // the 8 lanes of a write cycle hit 8 distinct bank groups)

@@ -373,6 +373,34 @@ def test_matmul_split_k_stays_in_bounds(m, n, k):
             assert np.array_equal(got[: m * n].view(np.uint32), first.view(np.uint32))
 
 
+@pytest.mark.parametrize("m,n,k,route", [(1500, 1280, 5120, "wide128"), (93, 3072, 5120, None),
+                                         (375, 1280, 1280, None), (100, 1030, 4096, None),
+                                         (40, 3072, 9216, "skinny")])
+def test_matmul_fold_sums_slices_in_order(m, n, k, route):
+    """The K split's fold: Y is bit for bit the float32 sum, in split order
+    0, 1, ..., of the partial slices the call left in the workspace (the
+    wide kernel at every tile height it takes here, ragged N, the skinny
+    kernel), on two calls in a row; the result meets the oracle's bound."""
+    qb_h = O.quantize_q4_0(_rand_w(n, k, 41 + m))
+    x_h = _rand_x(m, k, 43 + n)
+    ws = q4.matmul_workspace(m, n, k, "cuda")
+    got_route, splits = q4.matmul_route(m, n, k, ws.numel())
+    assert splits > 1 and (route is None or got_route == route), (got_route, splits)
+    assert ws.numel() == splits * m * n * 4
+    qb, x = dev(qb_h), dev(x_h)
+    for rep in range(2):
+        announce(f"matmul fold order {got_route} splits={splits} {m}x{n}x{k} call {rep}")
+        y = host(q4.matmul(qb, x, workspace=ws))
+        parts = host(ws).view(np.float32).reshape(splits, m, n)
+        acc = parts[0].copy()
+        for s in range(1, splits):
+            acc += parts[s]
+        assert np.array_equal(y.view(np.uint32), acc.view(np.uint32)), \
+            f"{int((y.view(np.uint32) != acc.view(np.uint32)).sum())} elements differ"
+    ref, b = O.matmul_f64(qb_h, x_h, n, k)
+    assert_within(y, ref, b, *MF, f"fold {got_route} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m", [16, 38, 76])
 def test_matmul_decoder_prefix_full(m):
     """The decoder projection set at the prefix lengths 16 / 38 / 76."""

@@ -396,6 +396,30 @@ def main():
                                        F16_PEAK_TFLOPS * 1e6)},
         "frac_of_peak_whole_layer": round(enc_tflops / F16_PEAK_TFLOPS, 4),
         "per_projection": enc_rows}
+    # the 1280-wide encoder projections with the residual add fused into the
+    # product (q4_matmul_residual) against q4_matmul followed by a separate add
+    res_rows = {}
+    for t, (name, n, k) in enumerate(synth.ENCODER_LAYER):
+        if n != 1280:
+            continue
+        w = encode(n, k, synth.seed_for(4, t))
+        r = copies_for(weight_bytes(n, k))
+        wc = [w] + [w.clone() for _ in range(r - 1)]
+        x = torch.from_numpy(synth.activations(m_enc, k, synth.seed_for(4, 10 + t))).cuda()
+        resid = torch.from_numpy(synth.activations(m_enc, n, synth.seed_for(4, 20 + t))).cuda()
+        y = torch.empty((m_enc, n), device="cuda")
+        ws = q4.matmul_residual_workspace(m_enc, n, k, "cuda")
+        fused = timed(lambda i: q4.matmul_residual(wc[i % r], x, resid, out=y, workspace=ws,
+                                                   stream=stream), r)
+
+        def unfused(i):
+            q4.matmul(wc[i % r], x, out=y, workspace=ws, stream=stream)
+            with torch.cuda.stream(stream):
+                torch.add(y, resid, out=y)
+        res_rows[f"{name}_M{m_enc}_{n}x{k}"] = {"fused_us": round(fused, 3),
+                                                 "matmul_then_add_us": round(timed(unfused, r), 3)}
+        del wc, w, x, resid, y, ws
+    rows[f"encoder_residual_M{m_enc}"] = res_rows
     for m in (375, 3000):
         r, f, u = gemm_set(enc_shapes, lambda nm, m=m: m // 4 if nm == "adapter" else m, 4)
         rows[f"encoder_M{m}"] = dict(r, layer_tflops=round(f / (u * 1e-6) / 1e12, 2))

@@ -145,6 +145,29 @@ q4_status q4_matmul(const void* w_q4, const float* x, float* y,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * q4_matmul_residual -- a projection with the residual add fused into its
+ * epilogue (section "Architecture": in the encoder of width 1280 the
+ * attention output and feed-forward down projections, 1280 outputs wide,
+ * feed the residual stream): y = r + X * deq(W)^T.
+ *   r : [M, N] float32 (device); either y itself (y += X deq(W)^T in
+ *       place) or a buffer that does not overlap y.
+ *   The other arguments are those of q4_matmul.
+ * Bit for bit, y[m, n] = r[m, n] + p[m, n] rounded once in float32, where p
+ * is what q4_matmul returns for the same arguments and workspace size.  The
+ * add rides in a kernel of the product -- the wide kernel's stores (routes
+ * "wide128" to "wide32" of q4_matmul_route, the encoder and adapter shapes)
+ * or, with a K split, the fold -- and in a second launch after the finished
+ * product on the other routes, where in place the product waits in the
+ * workspace (M*N*4 bytes, else Q4_ERR_WORKSPACE).
+ * q4_matmul_residual_workspace_bytes(M, N, K) covers every case on the
+ * current device.
+ */
+size_t q4_matmul_residual_workspace_bytes(int64_t M, int64_t N, int64_t K);
+q4_status q4_matmul_residual(const void* w_q4, const float* x, const float* r, float* y,
+                             int64_t M, int64_t N, int64_t K,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * q4_embed_rows -- token-embedding lookup (section "Solutions techniques pour
  * l'exécution dans le navigateur", item 3): out[i, :] = deq(T[ids[i], :]).
  *   table_q4 : N rows of Q4_0 (N = vocabulary size, K = model width).

@@ -8,6 +8,7 @@ fallback: if the library is not built, every entry point raises.
 Entry points (same names as the C ABI, minus the ``q4_`` prefix):
     matvec(w_q4, x, out=None)                    y = deq(W) x          (M <= 8)
     matmul(w_q4, x, out=None, workspace=True)    Y = X deq(W)^T        (matrix cores)
+    matmul_residual(w_q4, x, r, out=None, ...)   Y = R + X deq(W)^T   (fused epilogue)
     embed_rows(table_q4, ids, out=None)          rows of deq(T)
     lmhead_argmax(w_q4, x, workspace=None, ...)  argmax_n (deq(T) x)_n
     quantize(w, out=None, check=True)            float32 -> Q4_0 bytes
@@ -57,6 +58,8 @@ _SIGS = {
     "q4_matvec": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "q4_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
+    "q4_matmul_residual_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q4_matmul_residual": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
     "q4_embed_rows": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "q4_lmhead_argmax_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4_lmhead_argmax": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], ctypes.c_int),
@@ -206,6 +209,42 @@ def matmul(w_q4: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib().q4_matmul(_ptr(w_q4), _ptr(x2), _ptr(out), m, n, k, _ptr(workspace), ws_bytes,
                                _stream(stream)), "q4_matmul")
+    return out
+
+
+def matmul_residual_workspace(m: int, n: int, k: int, device) -> torch.Tensor | None:
+    """A workspace that covers matmul_residual for the shape on the current
+    device, in place or not (None if none is needed)."""
+    nbytes = int(lib().q4_matmul_residual_workspace_bytes(m, n, k))
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def matmul_residual(w_q4: torch.Tensor, x: torch.Tensor, r: torch.Tensor,
+                    out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None | bool = True, stream=None):
+    """Y = R + X deq(W)^T, the add fused into the product's epilogue where
+    the route allows (bit for bit R + matmul(...) in float32).  ``out`` may be
+    ``r`` itself (in place).  ``workspace`` as for matmul; ``True`` allocates
+    what the shape needs, in place included."""
+    n, k = q4_shape(w_q4)
+    x2 = _as_2d_f32(x, k)
+    m = x2.shape[0]
+    if r.dtype != torch.float32 or tuple(r.shape) != (m, n) or not r.is_contiguous():
+        raise ValueError(f"r must be a contiguous float32 [{m}, {n}] tensor")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        if workspace is True:
+            workspace = matmul_residual_workspace(m, n, k, x.device)
+        elif workspace is False:
+            workspace = None
+        _need_cuda(w_q4, x2, r, out, workspace)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().q4_matmul_residual(_ptr(w_q4), _ptr(x2), _ptr(r), _ptr(out), m, n, k,
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+               "q4_matmul_residual")
     return out
 
 

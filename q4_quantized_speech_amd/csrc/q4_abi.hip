@@ -98,9 +98,31 @@ q4_status q4_matmul(const void* w_q4, const float* x, float* y, int64_t M, int64
   if (!matmul_shape_ok(M, N, K)) return Q4_ERR_SHAPE;
   if (!aligned16(w_q4) || !aligned16(x) || !aligned16(y) || (workspace && !aligned16(workspace)))
     return Q4_ERR_ALIGN;
-  return hip_status(launch_matmul(static_cast<const uint8_t*>(w_q4), x, y, M, N, K, workspace,
-                                  workspace ? ws_bytes : 0, device_info().cu_count,
+  return hip_status(launch_matmul(static_cast<const uint8_t*>(w_q4), x, y, nullptr, M, N, K,
+                                  workspace, workspace ? ws_bytes : 0, device_info().cu_count,
                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t q4_matmul_residual_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!matmul_shape_ok(M, N, K)) return 0;
+  return matmul_residual_workspace_bytes(M, N, K, device_info().cu_count);
+}
+
+q4_status q4_matmul_residual(const void* w_q4, const float* x, const float* r, float* y,
+                             int64_t M, int64_t N, int64_t K, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (!w_q4 || !x || !r || !y) return Q4_ERR_NULL;
+  if (!matmul_shape_ok(M, N, K)) return Q4_ERR_SHAPE;
+  if (!aligned16(w_q4) || !aligned16(x) || !aligned16(r) || !aligned16(y) ||
+      (workspace && !aligned16(workspace)))
+    return Q4_ERR_ALIGN;
+  const size_t wsb = workspace ? ws_bytes : 0;
+  const int cus = device_info().cu_count;
+  if (r == y && !matmul_residual_fused(M, N, K, wsb, cus) &&
+      wsb < static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float))
+    return Q4_ERR_WORKSPACE;
+  return hip_status(launch_matmul(static_cast<const uint8_t*>(w_q4), x, y, r, M, N, K, workspace,
+                                  wsb, cus, static_cast<hipStream_t>(stream)));
 }
 
 q4_status q4_embed_rows(const void* table_q4, const int32_t* ids, float* out, int64_t M, int64_t N,

@@ -32,9 +32,14 @@ const char* matvec_route(int64_t N, int64_t K, bool argmax);
 // its K split count.
 const char* matmul_route(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int cus, int* splits);
 
-hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
-                         int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s);
+// r (nullable): y = r + the product (r is y or does not overlap it); an
+// unfused route in place needs M*N floats of workspace for the product.
+hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, const float* r, int64_t M,
+                         int64_t N, int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s);
 size_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
+// Whether the residual add rides in a kernel of the product for this plan.
+bool matmul_residual_fused(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int cus);
+size_t matmul_residual_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus);
 // M <= 4, K % 64 == 0: pps (pairs of blocks per K split) a multiple of 4
 // when splits > 1; partials [splits][M][N] in P, folded by the caller.
 int matmul_small_per_cu();

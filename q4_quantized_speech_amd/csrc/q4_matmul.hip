@@ -397,11 +397,15 @@ constexpr int WS_CONS = 256, WS_PT = 256, WS_THREADS = WS_CONS + WS_PT;
 constexpr int WS_WU = 9;                       // code dwords per producer thread: one pair
 static_assert(WS_PT == WS_BN, "one weight row per producer thread");
 
-template <int BM>
-__global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
-                       float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
-                       int tiles_n, int ntiles, int split_stages) {
+// RES (no K split): Y = R + the product, the add in float32 after the
+// accumulation, R read at the offsets Y is written (R may be Y itself).  The
+// kernels below wrap this body: the plain one keeps Y restrict-qualified
+// (without it the compiler scheduled the main loop differently, 1-2 %
+// slower), the residual one cannot (R may be Y).
+template <int BM, bool RES>
+__device__ __forceinline__ void ws_body(const uint8_t* __restrict__ W, const float* __restrict__ X,
+                                        float* Y, float* P, const float* R, int M, int N, int K,
+                                        int tiles_n, int ntiles, int split_stages) {
   constexpr int MI = BM / 16;                 // 16-row tiles of X
   constexpr int XU = BM * 16 / WS_PT;         // 16-byte X chunks per producer thread
   static_assert(BM % 32 == 0 && BM >= 32 && BM <= 128, "X is loaded in rounds of 32 rows");
@@ -477,16 +481,50 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       const __amdgpu_buffer_rsrc_t yrs =
           make_rsrc(out + static_cast<int64_t>(m0) * N, static_cast<int64_t>(rows) * N * 4);
       const int cb = (n0 + wave * 64 + (lane & 15)) * 4;
+      if constexpr (RES) {
+        // the residual tile in groups of 4 row tiles (64 values per lane),
+        // each group's loads in flight together before its adds and stores
+        const __amdgpu_buffer_rsrc_t rrs =
+            make_rsrc(R + static_cast<int64_t>(m0) * N, static_cast<int64_t>(rows) * N * 4);
+        constexpr int GI = MI < 4 ? MI : 4;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
+        for (int i0 = 0; i0 < MI; i0 += GI) {
+          float rv[GI][4][4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int ro = (i * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
+          for (int ii = 0; ii < GI; ++ii)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float val = acc[i][j][v];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0,
-                                                  WRITE_THROUGH);
+            for (int v = 0; v < 4; ++v) {
+              const int ro = ((i0 + ii) * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                rv[ii][v][j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rrs, ro + j * 64, 0, 0));
+            }
+#pragma unroll
+          for (int ii = 0; ii < GI; ++ii)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int ro = ((i0 + ii) * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float val = acc[i0 + ii][j][v] + rv[ii][v][j];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0,
+                                                      WRITE_THROUGH);
+              }
+            }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int ro = (i * 16 + (lane >> 4) * 4 + v) * N * 4 + cb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float val = acc[i][j][v];
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), yrs, ro + j * 64, 0,
+                                                    WRITE_THROUGH);
+            }
           }
         }
       }
@@ -501,7 +539,12 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int col = n0 + wave * 64 + j * 16 + (lane & 15);
-            if (col < N) yr[col] = acc[i][j][v];
+            if (col < N) {
+              if constexpr (RES)
+                yr[col] = acc[i][j][v] + R[static_cast<int64_t>(row) * N + col];
+              else
+                yr[col] = acc[i][j][v];
+            }
           }
         }
       }
@@ -598,6 +641,23 @@ void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X
       if (t + I < nst) Q4_WSSTEP(I);
 #undef Q4_WSSTEP
   }
+}
+
+template <int BM>
+__global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void matmul_ws_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X,
+                      float* __restrict__ Y, float* __restrict__ P, int M, int N, int K,
+                      int tiles_n, int ntiles, int split_stages) {
+  ws_body<BM, false>(W, X, Y, P, nullptr, M, N, K, tiles_n, ntiles, split_stages);
+}
+
+// Y = R + X deq(W)^T without a K split; R may be Y.
+template <int BM>
+__global__ __launch_bounds__(WS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void matmul_ws_res_kernel(const uint8_t* __restrict__ W, const float* __restrict__ X, float* Y,
+                          const float* R, int M, int N, int K, int tiles_n, int ntiles,
+                          int split_stages) {
+  ws_body<BM, true>(W, X, Y, nullptr, R, M, N, K, tiles_n, ntiles, split_stages);
 }
 
 // ---------------------------------------------------------------------------
@@ -808,9 +868,11 @@ __global__ __launch_bounds__(SK_THREADS) void matmul_skinny_kernel(
 // just written by workgroups on every XCD, so each read goes out to memory,
 // and a chain of dependent load-then-add steps would pay that latency once
 // per slice (measured ~4 us per call on the prefix shapes, mostly waiting).
-template <int S>
-__global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restrict__ P,
-                                                          float* __restrict__ Y, int64_t mn) {
+// RES: Y = R + the sum (R may be Y itself); with S == 1 it is the
+// residual add alone (P the product).
+template <int S, bool RES>
+__global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restrict__ P, float* Y,
+                                                          const float* R, int64_t mn) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   if ((mn & 3) == 0) {
     const int64_t n4 = mn >> 2;
@@ -823,6 +885,7 @@ __global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restric
       f32x4 a = v[0];
 #pragma unroll
       for (int s = 1; s < S; ++s) a += v[s];
+      if constexpr (RES) a += reinterpret_cast<const f32x4*>(R)[i];
       y4[i] = a;
     }
   } else {
@@ -833,19 +896,24 @@ __global__ __launch_bounds__(256) void splitk_fold_kernel(const float* __restric
       float a = v[0];
 #pragma unroll
       for (int s = 1; s < S; ++s) a += v[s];
+      if constexpr (RES) a += R[i];
       Y[i] = a;
     }
   }
 }
 
 template <int S>
-void launch_fold(const float* P, float* y, int64_t mn, int splits, int blocks, hipStream_t s) {
+void launch_fold(const float* P, float* y, const float* r, int64_t mn, int splits, int blocks,
+                 hipStream_t s) {
   if constexpr (S <= MAX_SPLITS) {
     if (splits == S) {
-      hipLaunchKernelGGL(splitk_fold_kernel<S>, dim3(blocks), dim3(256), 0, s, P, y, mn);
+      if (r)
+        hipLaunchKernelGGL((splitk_fold_kernel<S, true>), dim3(blocks), dim3(256), 0, s, P, y, r, mn);
+      else
+        hipLaunchKernelGGL((splitk_fold_kernel<S, false>), dim3(blocks), dim3(256), 0, s, P, y, r, mn);
       return;
     }
-    launch_fold<S + 1>(P, y, mn, splits, blocks, s);
+    launch_fold<S + 1>(P, y, r, mn, splits, blocks, s);
   }
 }
 
@@ -1117,10 +1185,63 @@ static void launch_skinny(const uint8_t* w, const float* x, float* y, float* P, 
                      groups, stages);
 }
 
-hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, int64_t N,
-                         int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
+template <int BM>
+static void launch_ws(const uint8_t* w, const float* x, float* y, float* P, const float* r,
+                      int64_t M, int64_t N, int64_t K, int splits, int stages, hipStream_t s) {
+  const int tiles_n = static_cast<int>((N + WS_BN - 1) / WS_BN);
+  const int ntiles = tiles_n * static_cast<int>((M + BM - 1) / BM);
+  // the residual rides in these stores only without a K split (else in the fold)
+  if (r != nullptr && P == nullptr)
+    hipLaunchKernelGGL(matmul_ws_res_kernel<BM>, dim3(ntiles), dim3(WS_THREADS), 0, s, w, x, y, r,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
+                       ntiles, stages);
+  else
+    hipLaunchKernelGGL(matmul_ws_kernel<BM>, dim3(ntiles * splits), dim3(WS_THREADS), 0, s, w, x, y,
+                       P, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
+                       ntiles, stages);
+}
+
+static bool is_wide(MatmulKind k) {
+  return k == MM_WIDE || k == MM_WIDE96 || k == MM_WIDE64 || k == MM_WIDE32;
+}
+
+// Whether Y = R + product adds R inside a kernel of the product: in the
+// wide kernel's stores (no K split) or in the fold (any K split); else a
+// second launch adds it to the finished product.
+static bool residual_fused(const MatmulPlan& p) { return p.splits > 1 || is_wide(p.kind); }
+
+bool matmul_residual_fused(int64_t M, int64_t N, int64_t K, size_t ws_bytes, int cus) {
+  return residual_fused(plan_matmul(M, N, K, cus, ws_bytes));
+}
+
+size_t matmul_residual_workspace_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  const MatmulPlan p = plan_matmul(M, N, K, cus, SIZE_MAX);
+  const size_t split = p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
+  // in place on an unfused route the product waits in the workspace
+  const size_t temp = residual_fused(p) ? 0 : static_cast<size_t>(M) * N * sizeof(float);
+  return std::max(split, temp);
+}
+
+hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, const float* r, int64_t M,
+                         int64_t N, int64_t K, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
   const MatmulPlan p = plan_matmul(M, N, K, cus, ws ? ws_bytes : 0);
   if (p.splits > MAX_SPLITS) return hipErrorInvalidValue;  // the planner caps it; the fold relies on it
+  const int64_t mn = M * N;
+  auto fold_blocks = [&]() {
+    const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
+    return static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
+  };
+  if (r != nullptr && !residual_fused(p)) {
+    // No K split, so the product kernel leaves the workspace alone: in place
+    // (R is Y) the product goes there, else straight to Y; then Y = R + it.
+    float* dst = r == y ? static_cast<float*>(ws) : y;
+    if (dst == nullptr || (r == y && ws_bytes < static_cast<size_t>(mn) * sizeof(float)))
+      return hipErrorInvalidValue;  // the entry point checks this first
+    const hipError_t e = launch_matmul(w, x, dst, nullptr, M, N, K, ws, ws_bytes, cus, s);
+    if (e != hipSuccess) return e;
+    launch_fold<1>(dst, y, r, mn, 1, fold_blocks(), s);
+    return hipGetLastError();
+  }
   float* P = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
   switch (p.kind) {
     case MM_STREAM:
@@ -1138,30 +1259,17 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
       }
       break;
     case MM_WIDE:
-    case MM_WIDE96:
-    case MM_WIDE64:
-    case MM_WIDE32: {
-      const int bm = p.kind == MM_WIDE ? 128 : p.kind == MM_WIDE96 ? 96 : p.kind == MM_WIDE64 ? 64 : 32;
-      const int tiles_n = static_cast<int>((N + WS_BN - 1) / WS_BN);
-      const int ntiles = tiles_n * static_cast<int>((M + bm - 1) / bm);
-      if (p.kind == MM_WIDE)
-        hipLaunchKernelGGL(matmul_ws_kernel<128>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
-                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), tiles_n, ntiles, p.stages);
-      else if (p.kind == MM_WIDE96)
-        hipLaunchKernelGGL(matmul_ws_kernel<96>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
-                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), tiles_n, ntiles, p.stages);
-      else if (p.kind == MM_WIDE64)
-        hipLaunchKernelGGL(matmul_ws_kernel<64>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
-                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), tiles_n, ntiles, p.stages);
-      else
-        hipLaunchKernelGGL(matmul_ws_kernel<32>, dim3(ntiles * p.splits), dim3(WS_THREADS), 0, s,
-                           w, x, y, P, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), tiles_n, ntiles, p.stages);
+      launch_ws<128>(w, x, y, P, r, M, N, K, p.splits, p.stages, s);
       break;
-    }
+    case MM_WIDE96:
+      launch_ws<96>(w, x, y, P, r, M, N, K, p.splits, p.stages, s);
+      break;
+    case MM_WIDE64:
+      launch_ws<64>(w, x, y, P, r, M, N, K, p.splits, p.stages, s);
+      break;
+    case MM_WIDE32:
+      launch_ws<32>(w, x, y, P, r, M, N, K, p.splits, p.stages, s);
+      break;
     case MM_TILE:
       launch_tile<128, 3>(w, x, y, P, M, N, K, p.splits, p.stages, s);
       break;
@@ -1176,10 +1284,7 @@ hipError_t launch_matmul(const uint8_t* w, const float* x, float* y, int64_t M, 
   if (p.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t mn = M * N;
-    const int64_t items = (mn & 3) == 0 ? mn / 4 : mn;
-    const int blocks = static_cast<int>(std::min<int64_t>((items + 255) / 256, 4 * cus));
-    launch_fold<2>(P, y, mn, p.splits, blocks, s);
+    launch_fold<2>(P, y, r, mn, p.splits, fold_blocks(), s);
   }
   return hipGetLastError();
 }

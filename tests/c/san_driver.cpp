@@ -44,12 +44,17 @@ const char* matmul_route(int64_t, int64_t, int64_t, size_t, int, int* splits) {
   if (splits) *splits = 1;
   return "stub";
 }
-hipError_t launch_matmul(const uint8_t*, const float*, float*, int64_t, int64_t, int64_t, void*,
-                         size_t, int, hipStream_t) {
+hipError_t launch_matmul(const uint8_t*, const float*, float*, const float*, int64_t, int64_t,
+                         int64_t, void*, size_t, int, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
 size_t matmul_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+// stub plan: the add is fused only for M > 48 (so small M in place needs workspace)
+bool matmul_residual_fused(int64_t M, int64_t, int64_t, size_t, int) { return M > 48; }
+size_t matmul_residual_workspace_bytes(int64_t M, int64_t N, int64_t, int) {
+  return M > 48 ? 0 : static_cast<size_t>(M * N) * sizeof(float);
+}
 int matmul_small_per_cu() { return 1; }
 void launch_matmul_small(const uint8_t*, const float*, float*, float*, int64_t, int64_t, int64_t,
                          int, int, hipStream_t) {}
@@ -146,6 +151,11 @@ static int run_abi() {
         q4_decode_chain(&one, 1, buf, a, b, buf, idx, buf, buf, ws, sizeof ws, nullptr);
       }
   }
+  // q4_matmul_residual: in place where the add is a second launch (the
+  // stub plan: M <= 48) needs M*N floats of workspace
+  EXPECT(q4_matmul_residual(buf, buf, buf, buf, 2, 16, 64, nullptr, 0, nullptr), Q4_ERR_WORKSPACE);
+  EXPECT(q4_matmul_residual(buf, buf, buf, buf, 2, 16, 64, ws, 2 * 16 * 4, nullptr), Q4_OK);
+  EXPECT(q4_matmul_residual(buf, buf, nullptr, buf, 2, 16, 64, ws, sizeof ws, nullptr), Q4_ERR_NULL);
   // q4_quantize
   EXPECT(q4_quantize(buf, ws, 4, 64, idx, nullptr), Q4_OK);
   EXPECT(q4_quantize(buf, ws, 4, 64, reinterpret_cast<int32_t*>(ws + 2), nullptr), Q4_ERR_ALIGN);
@@ -159,6 +169,8 @@ static int run_abi() {
         q4_matvec(buf, buf, buf, a, b, c, nullptr);
         q4_matmul(buf, buf, buf, a, b, c, nullptr, 0, nullptr);
         q4_matmul_workspace_bytes(a, b, c);
+        q4_matmul_residual(buf, buf, buf, buf, a, b, c, nullptr, 0, nullptr);
+        q4_matmul_residual_workspace_bytes(a, b, c);
         q4_matmul_route(a, b, c, 0, nullptr);
         q4_matvec_route(b, c, 1);
         q4_embed_rows(buf, idx, buf, a, b, c, nullptr);

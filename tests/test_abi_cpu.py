@@ -73,6 +73,28 @@ def test_matmul_workspace_validation():
     assert lib.q4_matmul_workspace_bytes(100, 200, 48) == 0
 
 
+def test_matmul_residual_validation():
+    """Checks that reject a call before anything is enqueued."""
+    lib = q4.lib()
+    f = lib.q4_matmul_residual
+    assert f(None, A, A, A, 4, 16, 64, None, 0, None) == q4.Q4_ERR_NULL
+    assert f(A, A, None, A, 4, 16, 64, None, 0, None) == q4.Q4_ERR_NULL   # r
+    assert f(A, A, A, None, 4, 16, 64, None, 0, None) == q4.Q4_ERR_NULL   # y
+    assert f(A, A, A, A, 4, 16, 48, None, 0, None) == q4.Q4_ERR_SHAPE
+    assert f(A, A, A + 4, A, 4, 16, 64, None, 0, None) == q4.Q4_ERR_ALIGN  # r
+    assert f(A, A, A, A, 4, 16, 64, A + 8, 1024, None) == q4.Q4_ERR_ALIGN  # workspace
+    # in place (r is y) where the add is a second launch: the product needs
+    # M*N floats of workspace
+    assert f(A, A, A, A, 2, 3072, 3072, None, 0, None) == q4.Q4_ERR_WORKSPACE
+    assert f(A, A, A, A, 2, 3072, 3072, A, 2 * 3072 * 4 - 16, None) == q4.Q4_ERR_WORKSPACE
+    w = lib.q4_matmul_residual_workspace_bytes
+    assert w(2, 3072, 3072) == 2 * 3072 * 4
+    # the encoder shapes add r inside the product's kernels: only the K split's workspace
+    assert w(1500, 1280, 1280) == lib.q4_matmul_workspace_bytes(1500, 1280, 1280) == 0
+    assert w(1500, 1280, 5120) == lib.q4_matmul_workspace_bytes(1500, 1280, 5120) > 0
+    assert w(0, 16, 64) == 0
+
+
 def test_matvec_m_range():
     f = q4.lib().q4_matvec
     assert f(A, A, A, 9, 16, 64, None) == q4.Q4_ERR_SHAPE

@@ -7,7 +7,9 @@ with NaN by ordinary kernels on the stream (not memset nodes) and other work
 runs on the stream; every replay is checked, not only the first, so a
 kernel that leaves state behind for the next call (the argmax's workspace,
 which its last workgroup clears; the no-allocation argmax's static scratch)
-would show on the second.  The shapes reach every q4_matmul route that a
+would show on the second; q4_matmul_residual is captured with its add in
+the wide kernel's stores, in the fold, and in a second launch.  The shapes
+reach every q4_matmul route that a
 graph of the model's calls would: the matvec kernel, stream16 (one tile and
 two binary16 parts of x), the small-M kernel, the skinny kernel and the wide
 kernel, the last two with a K split and its fold."""
@@ -57,6 +59,17 @@ def test_graph_replays_match_eager():
             calls.append((f"matmul {m}x{n}x{k} {route}",
                           lambda st, w=w, x=x, y=y, ws=ws: q4.matmul(w, x, out=y, workspace=ws,
                                                                      stream=st), [y]))
+        # the residual epilogue: fused in the wide kernel's stores (no K
+        # split), in the fold (K split), and as a second launch (matvec route)
+        for i, (m, n, k) in enumerate([(1500, 1280, 1280), (375, 1280, 5120), (2, 1000, 3072)]):
+            w, x = _w(n, k, 740 + i), _x(m, k, 750 + i)
+            rr = _x(m, n, 760 + i)
+            y = torch.empty((m, n), device="cuda")
+            ws = q4.matmul_residual_workspace(m, n, k, "cuda")
+            keep += [w, x, rr, ws]
+            calls.append((f"matmul_residual {m}x{n}x{k}",
+                          lambda st, w=w, x=x, rr=rr, y=y, ws=ws: q4.matmul_residual(
+                              w, x, rr, out=y, workspace=ws, stream=st), [y]))
         wv, xv = _w(3000, 3072, 700), _x(1, 3072, 701)[0]
         yv = torch.empty(3000, device="cuda")
         keep += [wv, xv]

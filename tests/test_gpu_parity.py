@@ -401,6 +401,69 @@ def test_matmul_fold_sums_slices_in_order(m, n, k, route):
     assert_within(y, ref, b, *MF, f"fold {got_route} {m}x{n}x{k}")
 
 
+# (M, N, K, route with the residual workspace): every q4_matmul route, the
+# wide tiles with and without a K split, ragged N on the wide kernel
+RESIDUAL_SHAPES = [
+    (1500, 1280, 5120, "wide128"), (1500, 1280, 1280, "wide32"), (3000, 1280, 1280, "wide64"),
+    (1500, 3840, 1280, "wide96"), (375, 1280, 1280, "wide32"), (93, 3072, 5120, None),
+    (300, 1282, 1024, None), (76, 3072, 9216, None), (40, 3072, 9216, "skinny"),
+    (16, 3072, 4096, "stream16"), (4, 3072, 9216, "small"), (3, 6144, 3072, "stream16"),
+    (2, 3072, 3072, "matvec"), (1, 3072, 4096, "matvec"), (200, 300, 1024, "tile"),
+    (130, 200, 96, "simple"), (8, 130, 12288, "skinny"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,route", RESIDUAL_SHAPES)
+def test_matmul_residual(m, n, k, route):
+    """q4_matmul_residual: Y = R + X deq(W)^T is bit for bit the float32 sum
+    of R and q4_matmul's own result (same workspace size) on every route,
+    out of place and in place (R is Y), and meets the oracle's bound plus
+    the final add's rounding."""
+    g = np.random.Generator(np.random.PCG64(m * 7 + n + k))
+    qb_h = O.quantize_q4_0((g.standard_normal((n, k)) * 0.02).astype(np.float32))
+    x_h = g.standard_normal((m, k)).astype(np.float32)
+    r_h = g.standard_normal((m, n)).astype(np.float32)
+    wq, x, r = dev(qb_h), dev(x_h), dev(r_h)
+    ws = q4.matmul_residual_workspace(m, n, k, "cuda")
+    nb = 0 if ws is None else ws.numel()
+    got_route = q4.matmul_route(m, n, k, nb)
+    assert route is None or got_route[0] == route, got_route
+    announce(f"matmul residual {m}x{n}x{k} {got_route}")
+    p = host(q4.matmul(wq, x, workspace=ws))
+    want = p + r_h                                   # float32, one rounding
+    y1 = host(q4.matmul_residual(wq, x, r, workspace=ws))
+    y2 = r.clone()
+    q4.matmul_residual(wq, x, y2, out=y2, workspace=ws)
+    y2 = host(y2)
+    for y, tag in ((y1, "out of place"), (y2, "in place")):
+        assert np.array_equal(y.view(np.uint32), want.view(np.uint32)), \
+            f"{tag}: {int((y.view(np.uint32) != want.view(np.uint32)).sum())} elements differ"
+    ref, b = O.matmul_f64(qb_h, x_h, n, k)
+    rel, ab = MV if m <= 4 else MF
+    tot = ref + r_h.astype(np.float64)
+    err = np.abs(y1.astype(np.float64) - tot)
+    assert np.all(err <= rel * b + ab + 2.0 ** -23 * np.abs(tot)), float(np.max(err))
+
+
+def test_matmul_residual_in_place_needs_workspace():
+    """In place on a route that adds R in a second launch, the product needs
+    M*N floats of workspace: without them the call is refused and Y is left
+    alone; with them it succeeds."""
+    m, n, k = 2, 3072, 3072
+    assert q4.matmul_route(m, n, k, 0)[0] == "matvec"
+    assert int(q4.lib().q4_matmul_residual_workspace_bytes(m, n, k)) == m * n * 4
+    qb = dev(O.quantize_q4_0(_rand_w(n, k, 51)))
+    x = dev(_rand_x(m, k, 52))
+    y = torch.full((m, n), 3.0, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.matmul_residual(qb, x, y, out=y, workspace=None)
+    assert e.value.status == q4.Q4_ERR_WORKSPACE
+    assert torch.all(y == 3.0)
+    q4.matmul_residual(qb, x, y, out=y, workspace=True)
+    want = host(q4.matmul(qb, x)) + np.float32(3.0)
+    assert np.array_equal(host(y).view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [16, 38, 76])
 def test_matmul_decoder_prefix_full(m):
     """The decoder projection set at the prefix lengths 16 / 38 / 76."""

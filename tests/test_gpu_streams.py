@@ -40,6 +40,9 @@ def test_entry_points_on_a_side_stream():
         enc = q4.quantize(wf, stream=side)
         yv = q4.matvec(wq, xd[:2], stream=side)
         ym = q4.matmul(wq, xd, stream=side)             # workspace allocated here
+        rr = torch.ones((m, n), device="cuda")
+        side.wait_stream(torch.cuda.current_stream())
+        yr = q4.matmul_residual(wq, xd, rr, stream=side)
         emb = q4.embed_rows(wq, idd, stream=side)
         idx, val = q4.lmhead_argmax(wq, xd[:3], stream=side)
         side.synchronize()
@@ -47,10 +50,12 @@ def test_entry_points_on_a_side_stream():
         ref, b = O.matmul_f64(qb, x, n, k)
         assert_within(yv.cpu().numpy(), ref[:2], b[:2], O.MATVEC_REL, O.MATVEC_ABS, "matvec side")
         assert_within(ym.cpu().numpy(), ref, b, O.MFMA_REL, O.MFMA_ABS, "matmul side")
+        assert np.array_equal(yr.cpu().numpy().view(np.uint32),
+                              (ym.cpu().numpy() + np.float32(1.0)).view(np.uint32))
         assert np.array_equal(emb.cpu().numpy(), O.embed_rows(qb, ids, n, k))
         for i in range(3):
             assert O.argmax_accepts(ref[i], b[i], int(idx[i].item()))
-        del enc, yv, ym, emb, idx, val                  # back to the side stream's pool
+        del enc, yv, ym, yr, rr, emb, idx, val          # back to the side stream's pool
     torch.cuda.synchronize()
 
 

@@ -21,9 +21,12 @@
  * repacked.
  *
  * Conventions for every entry point below.
- *  - Pointers named w_q4, table_q4, x, y, out, ids, workspace are DEVICE
+ *  - Pointers named w_q4, table_q4, x, r, y, out, ids, workspace are DEVICE
  *    pointers; the caller owns every buffer.  The library never allocates,
  *    frees or synchronises.
+ *  - Outputs and workspaces overlap neither the inputs nor each other, except
+ *    where an entry point allows it (q4_matmul_residual's r may be y;
+ *    q4_decode_chain's x may lie inside an earlier step's y).
  *  - All device pointers must be 16-byte aligned (Q4_ERR_ALIGN otherwise).
  *  - Dense matrices are row-major and contiguous: x is [M, K] floats, y is
  *    [M, N] floats.

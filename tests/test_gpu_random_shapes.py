@@ -1,7 +1,8 @@
 """Seeded random shapes through every entry point, each result against the
 oracle: rows of x from 1 to 400 (the matvec, small-M, skinny, tile and wide
 routes), any N up to 700, K any multiple of 32 up to 4096 (K % 64 == 32 takes
-the generic kernels), with and without a K-split workspace.  A second call
+the generic kernels), with and without a K-split workspace; and wider draws
+(N up to 12000, K up to 12288, M at every route's edges).  A second call
 must give the same bits.  The shapes are drawn, not chosen, so that edges
 nobody listed (a tile one row past a multiple, a single output column, a
 split that leaves a short last slice) are exercised too."""
@@ -45,6 +46,31 @@ def test_matmul_random_shape(seed):
         need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) if ws else 0
         route = q4.matmul_route(m, n, k, need)
         announce(f"random matmul seed={seed} {m}x{n}x{k} route={route}")
+        y1 = host(q4.matmul(wq, xd, workspace=ws))
+        y2 = host(q4.matmul(wq, xd, workspace=ws))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), route
+        assert_within(y1, ref, b, *(MV if m <= 4 else MF), f"seed={seed} {m}x{n}x{k} {route}")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_matmul_random_wide_shape(seed):
+    """Wider draws than above: rows of x at the routes' edges (1-4, 5, 16,
+    17, 48, 49, 80, 81, 128, 129 ... 400), N up to 12000 and K up to 12288,
+    K % 64 == 0 five times in six (the MFMA kernels), sizes capped so the
+    oracle stays fast."""
+    g = np.random.Generator(np.random.PCG64(20000 + seed))
+    m = int(g.choice([1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 76, 79,
+                      80, 81, 96, 97, 127, 128, 129, 200, 257, 300, 375, 383, 385, 400]))
+    k = 64 * int(g.integers(1, 193)) if g.random() < 0.85 else 32 * int(g.integers(1, 385))
+    nmax = max(1, min(12000, int(2.5e7 // k), int(6e8 // (m * k))))
+    n = int(g.integers(1, nmax + 1))
+    qb, x = _inputs(g, m, n, k)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    wq, xd = dev(qb), dev(x)
+    for ws in (True, None):
+        need = int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) if ws else 0
+        route = q4.matmul_route(m, n, k, need)
+        announce(f"random wide matmul seed={seed} {m}x{n}x{k} route={route}")
         y1 = host(q4.matmul(wq, xd, workspace=ws))
         y2 = host(q4.matmul(wq, xd, workspace=ws))
         assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), route

@@ -127,12 +127,13 @@ q4_status q4_matvec(const void* w_q4, const float* x, float* y,
  * scale exceeds 8188 in magnitude (largest |w| above 65504, which an encoder
  * only writes for weights that large) decodes to +-inf there.  M <= 4
  * (several decode streams) meets the q4_matvec bound, over q4_matvec's range
- * of x: either the rows of x go through the q4_matvec kernel (one or two
- * rows, K % 64 == 32, and, for three or four rows with K > 6144, weights
- * small enough that the rows' repeated reads stay in the caches:
- * (M - 1) * N * K * 18/32 bytes up to 40 MiB, K <= 12288), or the weights
- * are read once (by the persistent stream16 kernel for three or four rows
- * with K <= 6144, else by the small-M kernel) and enter the matrix cores
+ * of x: either the rows of x go through the q4_matvec kernel (one row; two
+ * rows unless K <= 3072 with 20 MiB of weights or more; K % 64 == 32; and,
+ * for three or four rows with K > 6144, weights small enough that the rows'
+ * repeated reads stay in the caches: (M - 1) * N * K * 18/32 bytes up to
+ * 40 MiB, K <= 12288), or the weights are read once (by the persistent
+ * stream16 kernel for three or four rows with K <= 6144 and for those two
+ * rows, else by the small-M kernel) and enter the matrix cores
  * exactly (q - 8, block scale applied in float32) with x as two binary16
  * parts after a power-of-two scaling per 256-value chunk of a row;
  * a chunk whose nonzero magnitudes span more than 2^20 (or reach 2^124) is
@@ -277,8 +278,9 @@ q4_status q4_lmhead_argmax_noalloc(const void* w_q4, const float* x, int32_t* ou
  * q4_matmul_route: the kernel q4_matmul runs for (M, N, K) with a workspace
  *   of ws_bytes on the current device -- "matvec" (the q4_matvec kernel,
  *   rows of x in pairs), "small" (M <= 4, weights read once), "stream16"
- *   (3 to 16 rows with K <= 6144, or up to 48 rows with K <= 3072: tiles of
- *   16 rows of x, weights read once), "skinny" (the other prompt-prefix
+ *   (3 to 16 rows with K <= 6144, up to 48 rows with K <= 3072, two rows
+ *   with K <= 3072 over 20 MiB of weights: tiles of 16 rows of x, weights
+ *   read once), "skinny" (the other prompt-prefix
  *   shapes up to 48 rows), "wide128" / "wide96" /
  *   "wide64" / "wide32" (tiles of 128, 96, 64 or 32 rows of X by 256
  *   outputs), "tile" (128 x 128, narrow outputs) or "simple" (K % 64 == 32)

@@ -1031,7 +1031,8 @@ struct MatmulPlan {
 // Up to 4 rows of x (decode streams) keep the float32 accuracy of q4_matvec.
 // Three or four rows with K <= 6144 take the stream16 kernel with x in two
 // binary16 parts (measured 16 % faster per decoder layer than the routes
-// below).  The matvec kernel (one set of workgroups per pair of rows of x,
+// below), and so do two rows with K <= 3072 over 20 MiB of weights or more.
+// The matvec kernel (one set of workgroups per pair of rows of x,
 // each weight read once per pair) serves one or two rows, any K % 64 == 32
 // and the shapes whose repeated weight reads stay in the caches ((M - 1) *
 // weight bytes up to STREAM_REREAD: measured faster there, it has no split
@@ -1047,12 +1048,19 @@ struct MatmulPlan {
 // at most MAX_SPLITS, for the skinny kernel no more partial bytes than weight
 // bytes, and never more than the workspace holds.
 constexpr int64_t STREAM_REREAD = int64_t{40} << 20;
+constexpr int64_t STREAM16_TWO_ROWS = int64_t{20} << 20;
 static MatmulPlan plan_matmul(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   if (M <= 4) {
     // three or four rows, K <= 6144: the stream16 kernel with x in two
     // binary16 parts (the q4_matvec bound), weights read once
     if (M >= 3 && matmul_stream16_chunks(M, K) > 0) return MatmulPlan{MM_STREAM16, 1, 0};
     const int64_t wbytes = N * (K / 32) * 18;
+    // two rows, K <= 3072, 20 MiB of weights or more: the same (measured
+    // against the pair kernel, same box, us: 12288 x 3072 9.4 / 10.1,
+    // 18432 x 3072 11.7 / 12.9, 131072 x 3072 49.0 / 58.2; below 20 MiB and
+    // for longer rows the pair kernel is as fast or faster)
+    if (M == 2 && K <= 3072 && wbytes >= STREAM16_TWO_ROWS && matmul_stream16_chunks(M, K) > 0)
+      return MatmulPlan{MM_STREAM16, 1, 0};
     if (M == 1 || K % 64 != 0 || (K <= 12288 && (M == 2 || (M - 1) * wbytes <= STREAM_REREAD)))
       return MatmulPlan{MM_STREAM, 1, 0};
   }

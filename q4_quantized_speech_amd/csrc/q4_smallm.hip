@@ -362,7 +362,7 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Three to 48 rows of x (a short prompt prefix, a few decode streams at
+// Two to 48 rows of x (a short prompt prefix, a few decode streams at
 // once): the product is still an HBM stream, and one 16 x 16 x 32 MFMA per
 // weight block and 16 rows of x carries them, so the work per weight is
 // nearly that of a single row.  The kernel has the matvec's shape: a
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 // streams 16 weight rows per pass:
 //  * x is converted once per workgroup to binary16 (round to nearest even)
 //    in the MFMA operand order (lane (m, g): row m of a 16-row tile of x,
-//    code group g), MT tiles of 16 rows; for three or four rows (HL) as two
+//    code group g), MT tiles of 16 rows; for two to four rows (HL) as two
 //    binary16 parts in one tile, described below;
 //  * lane (n, g) loads the contiguous 36-byte pair g of weight row n of each
 //    chunk (at one chunk per wave two passes in flight in two register
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(SM_THREADS) void matmul_small_kernel(
 constexpr int MS_MAX_MT = 3;   // tiles of 16 rows of x
 constexpr int MS_MAX_WAVES = 16;
 
-// HL (three or four rows of x, the q4_matvec bound): x is carried as two
+// HL (two to four rows of x, the q4_matvec bound): x is carried as two
 // binary16 parts, hi = RN(x s) and lo = RN(x s - hi), with s the power of two
 // that puts the largest magnitude of the row's 256-value chunk in
 // [2^14, 2^15) (undone in float32 after the chunk): hi in rows 0-3 of the
@@ -803,7 +803,7 @@ int matmul_small_per_cu() {
 // passes; measured slower than the skinny kernel on the 3072 x 9216 down
 // projection at 5 to 16 rows (13-14 against 11-12 us).
 int matmul_stream16_chunks(int64_t M, int64_t K) {
-  if (M < 3 || M > 16 * MS_MAX_MT || K % 64 != 0 || K <= 0) return 0;
+  if (M < 2 || M > 16 * MS_MAX_MT || K % 64 != 0 || K <= 0) return 0;
   const int64_t nchunk = (K + 255) / 256;
   if (M > 16) return nchunk <= 12 ? 1 : 0;
   if (nchunk <= MS_MAX_WAVES) return 1;

@@ -162,8 +162,10 @@ def test_header_is_plain_c(tmp_path):
 # each route reaches.
 ROUTES = [
     ((1, 18432, 3072), ("matvec", 1)),      # decode step
-    ((2, 18432, 3072), ("matvec", 1)),      # two streams: a pair of rows reads W once
-    ((2, 131072, 3072), ("matvec", 1)),     # at any size
+    ((2, 9216, 3072), ("matvec", 1)),       # two streams: a pair of rows reads W once
+    ((2, 12288, 4096), ("matvec", 1)),      # K past 3072: the pair kernel at any size
+    ((2, 18432, 3072), ("stream16", 1)),    # K <= 3072, 20 MiB of weights or more
+    ((2, 131072, 3072), ("stream16", 1)),
     ((4, 18432, 3072), ("stream16", 1)),    # four streams: x in two binary16 parts, weights once
     ((3, 3072, 4096), ("stream16", 1)),
     ((4, 3072, 9216), ("small", None)),     # K past 6144, large W: the small-M kernel

@@ -105,6 +105,44 @@ def test_small_m_x_range(case, k):
         assert np.all(y[2] == 0.0)
 
 
+@pytest.mark.parametrize("case", ["normal", "huge", "spread", "zero_row", "mixed_rows",
+                                  "outlier_1e11", "outlier_3e38", "huge_3e35"])
+def test_two_rows_stream16(case):
+    """Two rows of x over 20 MiB of weights with K <= 3072 take the stream16
+    kernel with x in two binary16 parts; they keep the q4_matvec bound over
+    x far from 1 (cases as in the x-range test above, rows 0 and 1)."""
+    m, n, k = 2, 12288, 3072
+    assert q4.matmul_route(m, n, k, 0) == ("stream16", 1)
+    g = np.random.Generator(np.random.PCG64(66))
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = g.standard_normal((m, k))
+    cols = [3, 77, k // 2 + 5, k - 1]
+    if case == "huge":
+        x *= 1e6
+    elif case == "spread":
+        x *= 1e-3
+        x[:, 77] = 1e4
+    elif case == "zero_row":
+        x[1] = 0.0
+    elif case == "mixed_rows":
+        x *= np.array([1e-20, 1e8])[:, None]
+    elif case.startswith("outlier"):
+        w[:, cols] = 0.0
+        x[:, cols] = float(case.split("_")[1])
+        x[1, cols] *= -1.0
+    elif case == "huge_3e35":
+        x *= 3e35
+        x[1] *= 1e-10
+    qb = O.quantize_q4_0(w)
+    x = x.astype(np.float32)
+    ref, b = O.matmul_f64(qb, x, n, k)
+    announce(f"two rows stream16 {case} {m}x{n}x{k}")
+    y = host(q4.matmul(dev(qb), dev(x)))
+    assert_within(y, ref, b, *MV, f"two rows {case}")
+    if case == "zero_row":
+        assert np.all(y[1] == 0.0)
+
+
 @pytest.mark.parametrize("m", [2, 3, 4])
 def test_small_m_decoder_layer(m):
     """The four decoder projections at their real shapes, all outputs."""
@@ -187,12 +225,12 @@ def test_stream16_tiles_edges(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 6144, 3072), (2, 300, 1088), (4, 300, 6208),
-                                   (3, 65, 1056), (2, 18432, 3072), (2, 65536, 3072),
+                                   (3, 65, 1056), (2, 9216, 3072), (2, 12288, 4096),
                                    (2, 3072, 9216)])
 def test_small_m_stream_route_is_matvec(m, n, k):
     """Where the rows go through the matvec kernel, q4_matmul returns exactly
     q4_matvec's bits (the same kernel, no workspace planned); two rows of x
-    take that route whatever the size of W (each pair reads W once)."""
+    take that route unless K <= 3072 with 20 MiB of weights or more."""
     assert int(q4.lib().q4_matmul_workspace_bytes(m, n, k)) == 0
     qb = dev(weights_q4(n, k, synth.seed_for(1, n + k)))
     x = dev(synth.activations(m, k, synth.seed_for(3, m + k)))

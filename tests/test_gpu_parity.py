@@ -402,10 +402,12 @@ def test_matmul_fold_sums_slices_in_order(m, n, k, route):
 
 
 # (M, N, K, route with the residual workspace): every q4_matmul route, the
-# wide tiles with and without a K split, ragged N on the wide kernel
+# wide tiles with and without a K split, ragged N on the wide kernel with
+# (its fold) and without a K split (its per-element stores)
 RESIDUAL_SHAPES = [
     (1500, 1280, 5120, "wide128"), (1500, 1280, 1280, "wide32"), (3000, 1280, 1280, "wide64"),
-    (1500, 3840, 1280, "wide96"), (375, 1280, 1280, "wide32"), (93, 3072, 5120, None),
+    (1500, 3840, 1280, "wide96"), (1500, 5120, 1280, "wide128"), (375, 1280, 1280, "wide32"),
+    (1500, 1300, 1280, "wide64"), (1000, 5000, 1280, "wide96"), (93, 3072, 5120, None),
     (300, 1282, 1024, None), (76, 3072, 9216, None), (40, 3072, 9216, "skinny"),
     (16, 3072, 4096, "stream16"), (4, 3072, 9216, "small"), (3, 6144, 3072, "stream16"),
     (2, 3072, 3072, "matvec"), (1, 3072, 4096, "matvec"), (200, 300, 1024, "tile"),

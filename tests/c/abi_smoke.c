@@ -25,6 +25,12 @@ int main(void) {
   if (q4_matvec(buf, buf, buf, 1, 1, 48, NULL) != Q4_ERR_SHAPE) return fail("matvec K % 32");
   if (q4_matmul(buf, buf, buf, 0, 1, 32, NULL, 0, NULL) != Q4_ERR_SHAPE) return fail("matmul M = 0");
   if (q4_matmul_workspace_bytes(0, 1, 32) != 0) return fail("matmul workspace of a bad shape");
+  if (q4_matmul_residual(buf, buf, NULL, buf, 1, 1, 32, NULL, 0, NULL) != Q4_ERR_NULL)
+    return fail("matmul_residual NULL r");
+  if (q4_matmul_residual(buf, buf, buf, buf, 2, 16, 64, NULL, 0, NULL) != Q4_ERR_WORKSPACE)
+    return fail("matmul_residual in place without workspace");
+  if (q4_matmul_residual_workspace_bytes(2, 16, 64) != 2 * 16 * 4)
+    return fail("matmul_residual workspace size");
   if (q4_embed_rows(buf, NULL, buf, 1, 1, 32, NULL) != Q4_ERR_NULL) return fail("embed NULL ids");
   if (q4_lmhead_argmax(buf, buf, idx, NULL, 1, 4, 32, NULL, 0, NULL) != Q4_ERR_WORKSPACE)
     return fail("lmhead without workspace");

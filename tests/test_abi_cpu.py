@@ -201,6 +201,30 @@ ROUTES = [
 ]
 
 
+def test_workspace_sizes_keep_the_plan():
+    """Over drawn shapes: the planned workspace gives exactly the plan an
+    unlimited one would (the K split it sizes for is the one taken), a
+    workspace of zero never splits, and the residual form's size covers
+    the plain one's (the same plan, plus room for an in-place product where
+    the add is a second launch)."""
+    import numpy as np
+    lib = q4.lib()
+    g = np.random.Generator(np.random.PCG64(123))
+    for _ in range(400):
+        m = int(g.choice([1, 2, 3, 4, 5, 16, 17, 48, 49, 80, 81, 129, 375, 1500, 3000]))
+        n = int(g.integers(1, 20000))
+        k = 32 * int(g.integers(1, 400))
+        need = int(lib.q4_matmul_workspace_bytes(m, n, k))
+        big = q4.matmul_route(m, n, k, 1 << 62)
+        assert q4.matmul_route(m, n, k, need) == big, (m, n, k, need)
+        assert need == (0 if big[1] == 1 else big[1] * m * n * 4), (m, n, k, need, big)
+        assert q4.matmul_route(m, n, k, 0)[1] == 1
+        rneed = int(lib.q4_matmul_residual_workspace_bytes(m, n, k))
+        assert rneed >= need
+        assert q4.matmul_route(m, n, k, rneed) == big, (m, n, k, rneed)
+        assert rneed in (need, m * n * 4), (m, n, k, rneed, need)
+
+
 @pytest.mark.parametrize("shape,want", ROUTES)
 def test_matmul_routing(shape, want):
     m, n, k = shape

@@ -447,6 +447,29 @@ def test_matmul_residual(m, n, k, route):
     assert np.all(err <= rel * b + ab + 2.0 ** -23 * np.abs(tot)), float(np.max(err))
 
 
+def test_matmul_residual_every_split_count():
+    """The fold adds R after the slices for every K-split count (2 to 16, a
+    workspace of s slices caps the split at s): bit for bit R plus
+    q4_matmul's result with the same workspace, in place."""
+    reached = set()
+    for (m, n, k) in [(96, 512, 12288), (8, 130, 12288)]:
+        qb = dev(O.quantize_q4_0(_rand_w(n, k, 61)))
+        x = dev(_rand_x(m, k, 62))
+        r_h = _rand_x(m, n, 63)
+        for s_ in range(2, 17):
+            nbytes = s_ * m * n * 4
+            route, splits = q4.matmul_route(m, n, k, nbytes)
+            assert 2 <= splits <= s_, (route, splits, s_)
+            reached.add(splits)
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+            announce(f"matmul residual split count {route} {splits} (cap {s_}) {m}x{n}x{k}")
+            want = host(q4.matmul(qb, x, workspace=ws)) + r_h
+            y = dev(r_h)
+            q4.matmul_residual(qb, x, y, out=y, workspace=ws)
+            assert np.array_equal(host(y).view(np.uint32), want.view(np.uint32)), (route, splits)
+    assert reached == set(range(2, 17)), sorted(reached)
+
+
 def test_matmul_residual_in_place_needs_workspace():
     """In place on a route that adds R in a second launch, the product needs
     M*N floats of workspace: without them the call is refused and Y is left
